@@ -1,0 +1,66 @@
+// Shared device-side helpers of the Lighthouse HIP library (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lh {
+
+constexpr int kMaxLevels = 16;
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+
+// Pyramid geometry of one head, passed by value to kernels.
+struct Geo {
+  int32_t N, d, p, L;
+  int32_t M, S, K, n_coarse, C;
+  int32_t log2p;                 // log2(p) when p is a power of two, else -1
+  int32_t base[kMaxLevels];      // flat index of the first entry of level l
+  int32_t pw[kMaxLevels];        // p^l
+  int32_t nlev[kMaxLevels];      // N / p^l
+};
+
+__device__ __forceinline__ int32_t div_pw(int32_t t, const Geo& g, int l) {
+  return g.log2p >= 0 ? (t >> (g.log2p * l)) : t / g.pw[l];
+}
+
+// ---- 8-element row slices (16 bytes of bf16, 32 bytes of fp32) ----------
+template <typename T> struct Row8;
+
+template <> struct Row8<float> {
+  static __device__ __forceinline__ void load(const float* p, float (&x)[8]) {
+    const f32x4 a = reinterpret_cast<const f32x4*>(p)[0];
+    const f32x4 b = reinterpret_cast<const f32x4*>(p)[1];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { x[e] = a[e]; x[e + 4] = b[e]; }
+  }
+  static __device__ __forceinline__ void store(float* p, const float (&x)[8]) {
+    f32x4 a, b;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { a[e] = x[e]; b[e] = x[e + 4]; }
+    reinterpret_cast<f32x4*>(p)[0] = a;
+    reinterpret_cast<f32x4*>(p)[1] = b;
+  }
+};
+
+template <> struct Row8<__bf16> {
+  static __device__ __forceinline__ void load(const __bf16* p, float (&x)[8]) {
+    const bf16x8 v = *reinterpret_cast<const bf16x8*>(p);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = static_cast<float>(v[e]);
+  }
+  // float -> bf16 rounds to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+  static __device__ __forceinline__ void store(__bf16* p, const float (&x)[8]) {
+    bf16x8 v;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = static_cast<__bf16>(x[e]);
+    *reinterpret_cast<bf16x8*>(p) = v;
+  }
+};
+
+__device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
+
+}  // namespace lh

@@ -1,0 +1,515 @@
+// C ABI of the Lighthouse library: host-side validation, buffer sizing and
+// the launch sequences of the forward and backward passes.  See
+// include/lighthouse.h for the contract of every entry point.
+#include "lighthouse.h"
+
+#include <algorithm>
+#include <string>
+
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+lh_status fail(lh_status s, const std::string& msg) {
+  g_err = msg;
+  return s;
+}
+
+lh_status hip_fail(hipError_t e, const char* where) {
+  return fail(LH_EHIP, std::string(where) + ": " + hipGetErrorString(e));
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct Stage {
+  int lvl0, lam, chunk;
+  int64_t rows_in, rows_out;
+  int out_buf;  // 0 = A, 1 = B, -1 = no f32 sums written
+};
+
+struct Plan {
+  lh::Geo g;
+  int64_t B, H, BH;
+  int dtype;
+  size_t es;
+  lh_sizes sz;
+  int nstages;
+  Stage st[lh::kMaxLevels];
+  size_t sums_rows[2];  // rows per head of the A / B f32 sum buffers
+};
+
+int lam_max(int p) {
+  int lam = 1;
+  int64_t pw = p;
+  while (lam < lh::kStageLevels && pw * p <= 64) {
+    pw *= p;
+    ++lam;
+  }
+  return lam;
+}
+
+lh_status make_plan(const lh_shape* s, Plan& P) {
+  g_err.clear();
+  if (!s) return fail(LH_EINVAL, "shape is null");
+  if (s->B < 1 || s->H < 1 || s->N < 1 || s->d < 1)
+    return fail(LH_EINVAL, "B, H, N and d must be positive");
+  if (s->dtype != LH_FP32 && s->dtype != LH_BF16) return fail(LH_EINVAL, "unknown dtype");
+  if (s->p < 2) return fail(LH_EINVAL, "pooling factor p must be >= 2");
+  if (s->L < 1) return fail(LH_EINVAL, "L must be >= 1");
+  if (s->L > lh::kMaxLevels) return fail(LH_EUNSUPPORTED, "L > 16 levels is not supported");
+  if (s->d != 64 && s->d != 128) return fail(LH_EUNSUPPORTED, "head dim must be 64 or 128");
+  lh::Geo& g = P.g;
+  int64_t pw = 1, M = 0;
+  for (int l = 0; l < s->L; ++l) {
+    if (l > 0) {
+      if (pw > s->N / s->p) return fail(LH_EINVAL, "N must be divisible by p^(L-1)");
+      pw *= s->p;
+    }
+    if (s->N % pw) return fail(LH_EINVAL, "N must be divisible by p^(L-1)");
+    g.pw[l] = (int32_t)pw;
+    g.nlev[l] = (int32_t)(s->N / pw);
+    g.base[l] = (int32_t)M;
+    M += s->N / pw;
+  }
+  for (int l = s->L; l < lh::kMaxLevels; ++l) {
+    g.pw[l] = 0;
+    g.nlev[l] = 0;
+    g.base[l] = (int32_t)M;
+  }
+  const int64_t nc = s->N / pw;
+  const int64_t BH = s->B * s->H;
+  if (BH * M >= (int64_t(1) << 31) || M * s->d >= (int64_t(1) << 31))
+    return fail(LH_EUNSUPPORTED, "B*H*M must stay below 2^31");
+  if (s->S < nc || s->S > M)
+    return fail(LH_EINVAL, "S must satisfy N/p^(L-1) <= S <= M (number of pyramid entries)");
+  g.N = (int32_t)s->N;
+  g.d = (int32_t)s->d;
+  g.p = s->p;
+  g.L = s->L;
+  g.M = (int32_t)M;
+  g.S = (int32_t)s->S;
+  g.n_coarse = (int32_t)nc;
+  g.C = (int32_t)(M - nc);
+  g.K = (int32_t)(s->S - nc);
+  g.log2p = -1;
+  for (int b = 0; b < 31; ++b)
+    if ((1 << b) == s->p) g.log2p = b;
+  P.B = s->B;
+  P.H = s->H;
+  P.BH = BH;
+  P.dtype = s->dtype;
+  P.es = s->dtype == LH_BF16 ? 2 : 4;
+
+  // pooling passes
+  P.nstages = 0;
+  P.sums_rows[0] = P.sums_rows[1] = 0;
+  if (s->L == 1) {
+    P.st[P.nstages++] = Stage{0, 0, 64, s->N, s->N, -1};
+  } else {
+    const int lm = lam_max(s->p);
+    int lvl = 0;
+    while (lvl < s->L - 1) {
+      const int lam = std::min(s->L - 1 - lvl, lm);
+      int64_t plam = 1;
+      for (int i = 0; i < lam; ++i) plam *= s->p;
+      const int64_t rep = std::max<int64_t>(1, 64 / plam);
+      const int64_t rows_in = s->N / g.pw[lvl];
+      Stage t{lvl, lam, (int)(plam * rep), rows_in, rows_in / plam, -1};
+      P.st[P.nstages++] = t;
+      lvl += lam;
+    }
+    for (int k = 0; k + 1 < P.nstages; ++k) {
+      P.st[k].out_buf = k % 2;
+      P.sums_rows[k % 2] = std::max<size_t>(P.sums_rows[k % 2], (size_t)P.st[k].rows_out);
+    }
+  }
+
+  lh_sizes& z = P.sz;
+  const size_t e = P.es, d = (size_t)s->d;
+  z.M = M;
+  z.C = M - nc;
+  z.K = s->S - nc;
+  z.n_coarse = nc;
+  z.bytes_qkv = (size_t)BH * s->N * d * e;
+  z.bytes_pyramid = (size_t)BH * (M - s->N) * d * e;
+  z.bytes_score = (size_t)BH * M * 4;
+  z.bytes_sel = (size_t)BH * z.K * 4;
+  z.bytes_sub_idx = (size_t)BH * s->S * 4;
+  z.bytes_pos = (size_t)BH * M * 4;
+  z.bytes_sub = (size_t)BH * s->S * d * e;
+  z.bytes_sub_f32 = (size_t)BH * s->S * d * 4;
+  z.bytes_lse = (size_t)BH * s->S * 4;
+  const size_t sums1 = align_up((size_t)BH * P.sums_rows[0] * d * 4) +
+                       align_up((size_t)BH * P.sums_rows[1] * d * 4);
+  z.ws_build_pyramid = 3 * sums1;
+  z.ws_score = 0;
+  z.ws_topk = z.K > 0 ? align_up(lh::topk_ws_bytes(BH, z.C)) : 0;
+  z.ws_gather = 0;
+  z.ws_attention_backward = align_up(z.bytes_lse);
+  z.ws_scatter_backward = sums1;
+  z.ws_forward = std::max(z.ws_build_pyramid, z.ws_topk);
+  z.ws_backward = align_up(z.bytes_sub) + 3 * align_up(z.bytes_sub_f32) + align_up(z.bytes_lse) +
+                  z.ws_scatter_backward;
+  return LH_OK;
+}
+
+// f32 sum buffers A and B inside a workspace, for tensor t.
+float* sums_ptr(const Plan& P, void* ws, int buf, int t) {
+  const size_t d = (size_t)P.g.d;
+  const size_t a = align_up((size_t)P.BH * P.sums_rows[0] * d * 4);
+  const size_t b = align_up((size_t)P.BH * P.sums_rows[1] * d * 4);
+  char* base = static_cast<char*>(ws) + (size_t)t * (a + b);
+  return reinterpret_cast<float*>(buf == 0 ? base : base + a);
+}
+
+lh_status check_ws(void* ws, size_t have, size_t need) {
+  if (need == 0) return LH_OK;
+  if (!ws) return fail(LH_EINVAL, "workspace pointer is null");
+  if (have < need)
+    return fail(LH_EWORKSPACE, "workspace too small: need " + std::to_string(need) + " bytes");
+  return LH_OK;
+}
+
+#define LH_NEED(ptr, name) \
+  if (!(ptr)) return fail(LH_EINVAL, name " is null")
+
+#define LH_HIP(call, where)                       \
+  do {                                            \
+    const hipError_t e_ = (call);                 \
+    if (e_ != hipSuccess) return hip_fail(e_, where); \
+  } while (0)
+
+lh_status run_pool(const Plan& P, const void* q, const void* k, const void* v, void* pq, void* pk,
+                   void* pv, float* score, void* ws, bool do_pool, bool do_score, hipStream_t st) {
+  const void* lvl0[3] = {q, k, v};
+  void* pyr[3] = {pq, pk, pv};
+  for (int s = 0; s < P.nstages; ++s) {
+    const Stage& t = P.st[s];
+    if (t.lam == 0 && !do_score) continue;
+    lh::PoolFwdArgs a{};
+    for (int i = 0; i < 3; ++i) {
+      if (s == 0) a.in[i] = lvl0[i];
+      else a.in[i] = do_pool ? sums_ptr(P, ws, P.st[s - 1].out_buf, i) : nullptr;
+      a.pyr[i] = do_pool ? pyr[i] : nullptr;
+      a.sums_out[i] = (do_pool && t.out_buf >= 0) ? sums_ptr(P, ws, t.out_buf, i) : nullptr;
+    }
+    a.score = do_score ? score : nullptr;
+    a.in_rows = t.rows_in;
+    a.out_rows = t.rows_out;
+    a.lvl0 = t.lvl0;
+    a.lam = t.lam;
+    a.chunk = t.chunk;
+    a.g = P.g;
+    LH_HIP(lh::launch_pool_fwd(a, P.dtype, P.BH, s == 0, do_pool, do_score, st), "pyramid");
+  }
+  return LH_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* lh_last_error(void) { return g_err.c_str(); }
+
+lh_status lh_query_sizes(const lh_shape* shape, lh_sizes* out) {
+  Plan P;
+  const lh_status s = make_plan(shape, P);
+  if (s != LH_OK) return s;
+  if (!out) return fail(LH_EINVAL, "sizes output is null");
+  *out = P.sz;
+  return LH_OK;
+}
+
+lh_status lh_build_pyramid(const lh_shape* shape, const void* q, const void* k, const void* v,
+                           void* pq, void* pk, void* pv, void* ws, size_t ws_bytes, void* stream) {
+  Plan P;
+  lh_status s = make_plan(shape, P);
+  if (s != LH_OK) return s;
+  LH_NEED(q, "q");
+  LH_NEED(k, "k");
+  LH_NEED(v, "v");
+  if (P.sz.bytes_pyramid) {
+    LH_NEED(pq, "pq");
+    LH_NEED(pk, "pk");
+    LH_NEED(pv, "pv");
+  }
+  if ((s = check_ws(ws, ws_bytes, P.sz.ws_build_pyramid)) != LH_OK) return s;
+  if (P.g.L == 1) return LH_OK;
+  return run_pool(P, q, k, v, pq, pk, pv, nullptr, ws, true, false,
+                  static_cast<hipStream_t>(stream));
+}
+
+lh_status lh_score(const lh_shape* shape, const void* q, const void* k, float* score, void* ws,
+                   size_t ws_bytes, void* stream) {
+  Plan P;
+  lh_status s = make_plan(shape, P);
+  if (s != LH_OK) return s;
+  LH_NEED(q, "q");
+  LH_NEED(k, "k");
+  LH_NEED(score, "score");
+  (void)ws;
+  (void)ws_bytes;
+  return run_pool(P, q, k, nullptr, nullptr, nullptr, nullptr, score, nullptr, false, true,
+                  static_cast<hipStream_t>(stream));
+}
+
+lh_status lh_topk(const lh_shape* shape, const float* score, int32_t* sel, void* ws,
+                  size_t ws_bytes, void* stream) {
+  Plan P;
+  lh_status s = make_plan(shape, P);
+  if (s != LH_OK) return s;
+  if (P.g.K == 0) return LH_OK;
+  LH_NEED(score, "score");
+  LH_NEED(sel, "sel");
+  if ((s = check_ws(ws, ws_bytes, P.sz.ws_topk)) != LH_OK) return s;
+  LH_HIP(lh::launch_topk(score, sel, ws, P.g, P.BH, static_cast<hipStream_t>(stream)), "topk");
+  return LH_OK;
+}
+
+lh_status lh_gather(const lh_shape* shape, const int32_t* sel, const void* q, const void* k,
+                    const void* v, const void* pq, const void* pk, const void* pv,
+                    int32_t* sub_idx, int32_t* pos, void* qs, void* ks, void* vs, void* ws,
+                    size_t ws_bytes, void* stream) {
+  Plan P;
+  lh_status s = make_plan(shape, P);
+  if (s != LH_OK) return s;
+  (void)ws;
+  (void)ws_bytes;
+  if (P.g.K > 0) LH_NEED(sel, "sel");
+  LH_NEED(q, "q");
+  LH_NEED(k, "k");
+  LH_NEED(v, "v");
+  if (P.sz.bytes_pyramid) {
+    LH_NEED(pq, "pq");
+    LH_NEED(pk, "pk");
+    LH_NEED(pv, "pv");
+  }
+  LH_NEED(sub_idx, "sub_idx");
+  LH_NEED(pos, "pos");
+  LH_NEED(qs, "qs");
+  LH_NEED(ks, "ks");
+  LH_NEED(vs, "vs");
+  const void* lv0[3] = {q, k, v};
+  const void* pyr[3] = {pq, pk, pv};
+  void* sub[3] = {qs, ks, vs};
+  LH_HIP(lh::launch_gather(sel, lv0, pyr, sub_idx, pos, sub, P.g, P.dtype, P.BH,
+                           static_cast<hipStream_t>(stream)),
+         "gather");
+  return LH_OK;
+}
+
+lh_status lh_attention(const lh_shape* shape, const void* qs, const void* ks, const void* vs,
+                       float* os, float* lse, void* stream) {
+  Plan P;
+  lh_status s = make_plan(shape, P);
+  if (s != LH_OK) return s;
+  LH_NEED(qs, "qs");
+  LH_NEED(ks, "ks");
+  LH_NEED(vs, "vs");
+  LH_NEED(os, "os");
+  LH_NEED(lse, "lse");
+  LH_HIP(lh::launch_attn_fwd(qs, ks, vs, os, lse, P.g.S, P.g.d, P.dtype, P.BH,
+                             static_cast<hipStream_t>(stream)),
+         "attention");
+  return LH_OK;
+}
+
+lh_status lh_scatter(const lh_shape* shape, const float* os, const int32_t* pos, void* out,
+                     void* stream) {
+  Plan P;
+  lh_status s = make_plan(shape, P);
+  if (s != LH_OK) return s;
+  LH_NEED(os, "os");
+  LH_NEED(pos, "pos");
+  LH_NEED(out, "out");
+  lh::BcastArgs a{};
+  a.src[0] = os;
+  a.out[0] = out;
+  a.pos = pos;
+  a.mean = 1;
+  a.g = P.g;
+  LH_HIP(lh::launch_bcast(a, P.dtype, 1, P.BH, static_cast<hipStream_t>(stream)),
+         "scatter");
+  return LH_OK;
+}
+
+lh_status lh_forward(const lh_shape* shape, const void* q, const void* k, const void* v,
+                     void* out, const lh_buffers* b, void* ws, size_t ws_bytes, void* stream) {
+  Plan P;
+  lh_status s = make_plan(shape, P);
+  if (s != LH_OK) return s;
+  LH_NEED(b, "buffers");
+  LH_NEED(q, "q");
+  LH_NEED(k, "k");
+  LH_NEED(v, "v");
+  LH_NEED(out, "out");
+  if (P.sz.bytes_pyramid) {
+    LH_NEED(b->pq, "buffers.pq");
+    LH_NEED(b->pk, "buffers.pk");
+    LH_NEED(b->pv, "buffers.pv");
+  }
+  LH_NEED(b->score, "buffers.score");
+  if (P.g.K > 0) LH_NEED(b->sel, "buffers.sel");
+  LH_NEED(b->sub_idx, "buffers.sub_idx");
+  LH_NEED(b->pos, "buffers.pos");
+  LH_NEED(b->qs, "buffers.qs");
+  LH_NEED(b->ks, "buffers.ks");
+  LH_NEED(b->vs, "buffers.vs");
+  LH_NEED(b->os, "buffers.os");
+  LH_NEED(b->lse, "buffers.lse");
+  if ((s = check_ws(ws, ws_bytes, P.sz.ws_forward)) != LH_OK) return s;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if ((s = run_pool(P, q, k, v, b->pq, b->pk, b->pv, b->score, ws, P.g.L > 1, true, st)) != LH_OK)
+    return s;
+  LH_HIP(lh::launch_topk(b->score, b->sel, ws, P.g, P.BH, st), "topk");
+  const void* lv0[3] = {q, k, v};
+  const void* pyr[3] = {b->pq, b->pk, b->pv};
+  void* sub[3] = {b->qs, b->ks, b->vs};
+  LH_HIP(lh::launch_gather(b->sel, lv0, pyr, b->sub_idx, b->pos, sub, P.g, P.dtype, P.BH, st),
+         "gather");
+  LH_HIP(lh::launch_attn_fwd(b->qs, b->ks, b->vs, b->os, b->lse, P.g.S, P.g.d, P.dtype, P.BH, st),
+         "attention");
+  lh::BcastArgs a{};
+  a.src[0] = b->os;
+  a.out[0] = out;
+  a.pos = b->pos;
+  a.mean = 1;
+  a.g = P.g;
+  LH_HIP(lh::launch_bcast(a, P.dtype, 1, P.BH, st), "scatter");
+  return LH_OK;
+}
+
+static lh_status run_scatter_bwd(const Plan& P, const void* dout, const int32_t* pos, void* dos,
+                                 void* ws, hipStream_t st) {
+  for (int s = 0; s < P.nstages; ++s) {
+    const Stage& t = P.st[s];
+    lh::PoolBwdArgs a{};
+    a.in = s == 0 ? dout : static_cast<const void*>(sums_ptr(P, ws, P.st[s - 1].out_buf, 0));
+    a.dos = dos;
+    a.sums_out = t.out_buf >= 0 ? sums_ptr(P, ws, t.out_buf, 0) : nullptr;
+    a.pos = pos;
+    a.in_rows = t.rows_in;
+    a.out_rows = t.rows_out;
+    a.lvl0 = t.lvl0;
+    a.lam = t.lam;
+    a.chunk = t.chunk;
+    a.g = P.g;
+    LH_HIP(lh::launch_pool_bwd(a, P.dtype, P.BH, s == 0, st), "scatter_backward");
+  }
+  return LH_OK;
+}
+
+lh_status lh_scatter_backward(const lh_shape* shape, const void* dout, const int32_t* pos,
+                              void* dos, void* ws, size_t ws_bytes, void* stream) {
+  Plan P;
+  lh_status s = make_plan(shape, P);
+  if (s != LH_OK) return s;
+  LH_NEED(dout, "dout");
+  LH_NEED(pos, "pos");
+  LH_NEED(dos, "dos");
+  if ((s = check_ws(ws, ws_bytes, P.sz.ws_scatter_backward)) != LH_OK) return s;
+  return run_scatter_bwd(P, dout, pos, dos, ws, static_cast<hipStream_t>(stream));
+}
+
+lh_status lh_attention_backward(const lh_shape* shape, const void* qs, const void* ks,
+                                const void* vs, const float* os, const float* lse, const void* dos,
+                                float* dqs, float* dks, float* dvs, void* ws, size_t ws_bytes,
+                                void* stream) {
+  Plan P;
+  lh_status s = make_plan(shape, P);
+  if (s != LH_OK) return s;
+  LH_NEED(qs, "qs");
+  LH_NEED(ks, "ks");
+  LH_NEED(vs, "vs");
+  LH_NEED(os, "os");
+  LH_NEED(lse, "lse");
+  LH_NEED(dos, "dos");
+  LH_NEED(dqs, "dqs");
+  LH_NEED(dks, "dks");
+  LH_NEED(dvs, "dvs");
+  if ((s = check_ws(ws, ws_bytes, P.sz.ws_attention_backward)) != LH_OK) return s;
+  LH_HIP(lh::launch_attn_bwd(qs, ks, vs, os, lse, dos, dqs, dks, dvs, static_cast<float*>(ws),
+                             P.g.S, P.g.d, P.dtype, P.BH, static_cast<hipStream_t>(stream)),
+         "attention_backward");
+  return LH_OK;
+}
+
+lh_status lh_gather_backward(const lh_shape* shape, const float* dqs, const float* dks,
+                             const float* dvs, const int32_t* pos, void* dq, void* dk, void* dv,
+                             void* stream) {
+  Plan P;
+  lh_status s = make_plan(shape, P);
+  if (s != LH_OK) return s;
+  LH_NEED(dqs, "dqs");
+  LH_NEED(dks, "dks");
+  LH_NEED(dvs, "dvs");
+  LH_NEED(pos, "pos");
+  LH_NEED(dq, "dq");
+  LH_NEED(dk, "dk");
+  LH_NEED(dv, "dv");
+  lh::BcastArgs a{};
+  a.src[0] = dqs;
+  a.src[1] = dks;
+  a.src[2] = dvs;
+  a.out[0] = dq;
+  a.out[1] = dk;
+  a.out[2] = dv;
+  a.pos = pos;
+  a.mean = 0;
+  a.g = P.g;
+  LH_HIP(lh::launch_bcast(a, P.dtype, 3, P.BH, static_cast<hipStream_t>(stream)),
+         "gather_backward");
+  return LH_OK;
+}
+
+lh_status lh_backward(const lh_shape* shape, const void* dout, const lh_buffers* b, void* dq,
+                      void* dk, void* dv, void* ws, size_t ws_bytes, void* stream) {
+  Plan P;
+  lh_status s = make_plan(shape, P);
+  if (s != LH_OK) return s;
+  LH_NEED(b, "buffers");
+  LH_NEED(dout, "dout");
+  LH_NEED(b->pos, "buffers.pos");
+  LH_NEED(b->qs, "buffers.qs");
+  LH_NEED(b->ks, "buffers.ks");
+  LH_NEED(b->vs, "buffers.vs");
+  LH_NEED(b->os, "buffers.os");
+  LH_NEED(b->lse, "buffers.lse");
+  LH_NEED(dq, "dq");
+  LH_NEED(dk, "dk");
+  LH_NEED(dv, "dv");
+  if ((s = check_ws(ws, ws_bytes, P.sz.ws_backward)) != LH_OK) return s;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  char* w = static_cast<char*>(ws);
+  void* dos = w;
+  w += align_up(P.sz.bytes_sub);
+  float* dqs = reinterpret_cast<float*>(w);
+  w += align_up(P.sz.bytes_sub_f32);
+  float* dks = reinterpret_cast<float*>(w);
+  w += align_up(P.sz.bytes_sub_f32);
+  float* dvs = reinterpret_cast<float*>(w);
+  w += align_up(P.sz.bytes_sub_f32);
+  float* delta = reinterpret_cast<float*>(w);
+  w += align_up(P.sz.bytes_lse);
+  if ((s = run_scatter_bwd(P, dout, b->pos, dos, w, st)) != LH_OK) return s;
+  LH_HIP(lh::launch_attn_bwd(b->qs, b->ks, b->vs, b->os, b->lse, dos, dqs, dks, dvs, delta, P.g.S,
+                             P.g.d, P.dtype, P.BH, st),
+         "attention_backward");
+  lh::BcastArgs a{};
+  a.src[0] = dqs;
+  a.src[1] = dks;
+  a.src[2] = dvs;
+  a.out[0] = dq;
+  a.out[1] = dk;
+  a.out[2] = dv;
+  a.pos = b->pos;
+  a.mean = 0;
+  a.g = P.g;
+  LH_HIP(lh::launch_bcast(a, P.dtype, 3, P.BH, st), "gather_backward");
+  return LH_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,280 @@
+// Pooling kernels: the forward pyramid with fused scores, and the scatter
+// backward, which is the same span reduction applied to dout / c_t.
+//
+// Symmetric average pooling follows the gist.science technical summary of
+// the Lighthouse paper, §2.A (levels of p consecutive entries, level 0 =
+// tokens) and the bitsgeniais post, phase 1.  Scores follow §2.B of the same
+// summary and phase 2 of the post: an l2 norm of q and of k per token, coarse
+// levels inheriting the max of their children.
+//
+// Mapping: a row of d elements is covered by d/8 lanes (8 elements each, one
+// 16-byte bf16 or 32-byte fp32 access); a 256-thread block holds 256/(d/8)
+// such row groups.  Each row group walks one chunk of consecutive input rows
+// in order and keeps one running float32 sum per level in registers, so each
+// input row is read exactly once and every level is produced in the same
+// pass.  Deep pyramids use several passes: a pass hands the float32 sums of
+// its top level to the next one.
+#include "kernels.h"
+
+namespace lh {
+
+namespace {
+
+// ||x||_2 of a d-long row spread over `lpr` lanes (element 8*lane + e in
+// x[e]), in the fixed float32 order: squares, then the halving tree
+// y[i] += y[i + w/2] for w = d, d/2, ..., 2 (cross-lane strides d/2..8 first,
+// then in-lane strides 4, 2, 1), then a correctly rounded square root.  No
+// fused multiply-add, so the result is reproducible bit for bit.
+__device__ __forceinline__ float row_norm(const float (&x)[8], int lpr) {
+#pragma clang fp contract(off)
+  float a[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) a[e] = x[e] * x[e];
+  for (int off = lpr >> 1; off >= 1; off >>= 1) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) a[e] = a[e] + __shfl_xor(a[e], off);
+  }
+  const float b0 = a[0] + a[4], b1 = a[1] + a[5], b2 = a[2] + a[6], b3 = a[3] + a[7];
+  const float c0 = b0 + b2, c1 = b1 + b3;
+  return sqrtf(c0 + c1);  // correctly rounded on gfx950 (not __fsqrt_rn)
+}
+
+__device__ __forceinline__ void scale8(float (&x)[8], float div, bool pow2) {
+  if (pow2) {
+    const float r = 1.0f / div;  // exact for powers of two
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] *= r;
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = x[e] / div;
+  }
+}
+
+// One pass over the tensors listed in `tid` for the chunk of rows
+// [r0, r0 + nrows) of head bh.  SCORE: 0 none, 1 norms (level 0 input),
+// 2 max-pool of stored level-lvl0 scores.
+template <typename Tin, typename Tout, int NT, int SCORE>
+__device__ __forceinline__ void pool_pass(const PoolFwdArgs& a, const int (&tid)[NT],
+                                          bool do_pool, int64_t bh, int64_t r0, int nrows,
+                                          int lane) {
+  const Geo& g = a.g;
+  const int d = g.d;
+  const int lpr = d / 8;
+  const bool pow2 = g.log2p >= 0;
+  const Tin* in[NT];
+  Tout* pyr[NT];
+  float* so[NT];
+#pragma unroll
+  for (int i = 0; i < NT; ++i) {
+    in[i] = a.in[tid[i]] ? static_cast<const Tin*>(a.in[tid[i]]) + bh * a.in_rows * d + 8 * lane
+                         : nullptr;  // score-only passes above level 0 read no rows
+    pyr[i] = do_pool ? static_cast<Tout*>(a.pyr[tid[i]]) + bh * (int64_t)(g.M - g.N) * d + 8 * lane
+                     : nullptr;
+    so[i] = a.sums_out[tid[i]] ? a.sums_out[tid[i]] + bh * a.out_rows * d + 8 * lane : nullptr;
+  }
+  float* score = a.score ? a.score + bh * g.M : nullptr;
+
+  float acc[kStageLevels][NT][8];
+  float smax[kStageLevels];
+  int cnt[kStageLevels];
+#pragma unroll
+  for (int l = 0; l < kStageLevels; ++l) {
+    smax[l] = neg_inf();
+    cnt[l] = 0;
+#pragma unroll
+    for (int i = 0; i < NT; ++i)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[l][i][e] = 0.f;
+  }
+
+  for (int r = 0; r < nrows; ++r) {
+    const int64_t row = r0 + r;
+    float x[NT][8];
+    if (SCORE == 1 || do_pool) {
+#pragma unroll
+      for (int i = 0; i < NT; ++i) Row8<Tin>::load(in[i] + row * d, x[i]);
+    }
+    float s = 0.f;
+    if constexpr (SCORE == 1) {
+      s = row_norm(x[0], lpr) + row_norm(x[1], lpr);
+      if (lane == 0) score[row] = s;
+    } else if constexpr (SCORE == 2) {
+      s = score[g.base[a.lvl0] + row];
+    }
+    if (do_pool) {
+#pragma unroll
+      for (int i = 0; i < NT; ++i)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[0][i][e] += x[i][e];
+    }
+    if constexpr (SCORE != 0) smax[0] = fmaxf(smax[0], s);
+
+#pragma unroll
+    for (int l = 0; l < kStageLevels; ++l) {
+      if (l >= a.lam) break;
+      if (++cnt[l] < g.p) break;
+      cnt[l] = 0;
+      const int lev = a.lvl0 + l + 1;                       // level just completed
+      const int64_t j = (row + 1) / g.pw[l + 1] - 1;        // its index in that level
+      if (do_pool) {
+#pragma unroll
+        for (int i = 0; i < NT; ++i) {
+          float m[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) m[e] = acc[l][i][e];
+          scale8(m, static_cast<float>(g.pw[lev]), pow2);
+          Row8<Tout>::store(pyr[i] + (int64_t)(g.base[lev] - g.N + j) * d, m);
+        }
+      }
+      if constexpr (SCORE != 0) {
+        if (lane == 0) score[g.base[lev] + j] = smax[l];
+      }
+      if (l + 1 < kStageLevels && l + 1 < a.lam) {
+        if (do_pool) {
+#pragma unroll
+          for (int i = 0; i < NT; ++i)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[(l + 1) % kStageLevels][i][e] += acc[l][i][e];
+        }
+        if constexpr (SCORE != 0)
+          smax[(l + 1) % kStageLevels] = fmaxf(smax[(l + 1) % kStageLevels], smax[l]);
+      } else if (do_pool && so[0] != nullptr) {
+#pragma unroll
+        for (int i = 0; i < NT; ++i) Row8<float>::store(so[i] + j * d, acc[l][i]);
+      }
+#pragma unroll
+      for (int i = 0; i < NT; ++i)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[l][i][e] = 0.f;
+      smax[l] = neg_inf();
+    }
+  }
+}
+
+template <typename Tin, typename Tout, bool FIRST>
+__global__ __launch_bounds__(256) void pool_fwd_kernel(PoolFwdArgs a, int do_pool, int do_score) {
+  const int lpr = a.g.d / 8;
+  const int rgs = 256 / lpr;
+  const int rg = threadIdx.x / lpr, lane = threadIdx.x % lpr;
+  const int64_t bh = blockIdx.y;
+  const int64_t nchunks = (a.in_rows + a.chunk - 1) / a.chunk;
+  const int64_t c = (int64_t)blockIdx.x * rgs + rg;
+  if (c >= nchunks) return;  // no block-wide barrier in this kernel
+  const int64_t r0 = c * a.chunk;
+  const int nrows = (int)min((int64_t)a.chunk, a.in_rows - r0);
+  constexpr int kScore = FIRST ? 1 : 2;
+  // pass 1: q and k (with the scores); pass 2: v
+  const int qk[2] = {0, 1};
+  if (do_score) {
+    pool_pass<Tin, Tout, 2, kScore>(a, qk, do_pool != 0, bh, r0, nrows, lane);
+  } else if (do_pool) {
+    pool_pass<Tin, Tout, 2, 0>(a, qk, true, bh, r0, nrows, lane);
+  }
+  if (do_pool) {
+    const int vv[1] = {2};
+    pool_pass<Tin, Tout, 1, 0>(a, vv, true, bh, r0, nrows, lane);
+  }
+}
+
+// Scatter backward: dos[pos(e)] = sum over tokens t of e's span of
+// dout[t] / c_t.  Same row-group walk as the forward; only selected entries
+// are written.
+template <typename Tin, typename Tout, bool FIRST>
+__global__ __launch_bounds__(256) void pool_bwd_kernel(PoolBwdArgs a) {
+  const Geo& g = a.g;
+  const int d = g.d;
+  const int lpr = d / 8;
+  const int rgs = 256 / lpr;
+  const int rg = threadIdx.x / lpr, lane = threadIdx.x % lpr;
+  const int64_t bh = blockIdx.y;
+  const int64_t nchunks = (a.in_rows + a.chunk - 1) / a.chunk;
+  const int64_t c = (int64_t)blockIdx.x * rgs + rg;
+  if (c >= nchunks) return;
+  const int64_t r0 = c * a.chunk;
+  const int nrows = (int)min((int64_t)a.chunk, a.in_rows - r0);
+  const Tin* in = static_cast<const Tin*>(a.in) + bh * a.in_rows * d + 8 * lane;
+  Tout* dos = static_cast<Tout*>(a.dos) + bh * (int64_t)g.S * d + 8 * lane;
+  float* so = a.sums_out ? a.sums_out + bh * a.out_rows * d + 8 * lane : nullptr;
+  const int32_t* pos = a.pos + bh * g.M;
+
+  float acc[kStageLevels][8];
+  int cnt[kStageLevels];
+#pragma unroll
+  for (int l = 0; l < kStageLevels; ++l) {
+    cnt[l] = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[l][e] = 0.f;
+  }
+  for (int r = 0; r < nrows; ++r) {
+    const int64_t row = r0 + r;
+    float x[8];
+    Row8<Tin>::load(in + row * d, x);
+    if constexpr (FIRST) {
+      const int t = (int)row;
+      int ct = 0;
+      for (int l = 0; l < g.L; ++l) ct += pos[g.base[l] + div_pw(t, g, l)] >= 0;
+      const float rc = 1.0f / static_cast<float>(ct);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] *= rc;
+      const int32_t pt = pos[t];
+      if (pt >= 0) Row8<Tout>::store(dos + (int64_t)pt * d, x);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[0][e] += x[e];
+#pragma unroll
+    for (int l = 0; l < kStageLevels; ++l) {
+      if (l >= a.lam) break;
+      if (++cnt[l] < g.p) break;
+      cnt[l] = 0;
+      const int lev = a.lvl0 + l + 1;
+      const int64_t j = (row + 1) / g.pw[l + 1] - 1;
+      const int32_t pe = pos[g.base[lev] + j];
+      if (pe >= 0) Row8<Tout>::store(dos + (int64_t)pe * d, acc[l]);
+      if (l + 1 < kStageLevels && l + 1 < a.lam) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[(l + 1) % kStageLevels][e] += acc[l][e];
+      } else if (so != nullptr) {
+        Row8<float>::store(so + j * d, acc[l]);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[l][e] = 0.f;
+    }
+  }
+}
+
+dim3 pool_grid(int64_t in_rows, int chunk, int d, int64_t BH) {
+  const int rgs = 256 / (d / 8);
+  const int64_t nchunks = (in_rows + chunk - 1) / chunk;
+  return dim3((unsigned)((nchunks + rgs - 1) / rgs), (unsigned)BH);
+}
+
+}  // namespace
+
+hipError_t launch_pool_fwd(const PoolFwdArgs& a, int dtype, int64_t BH, bool first,
+                           bool do_pool, bool do_score, hipStream_t st) {
+  const dim3 grid = pool_grid(a.in_rows, a.chunk, a.g.d, BH);
+  const int dp = do_pool, ds = do_score;
+  if (dtype == 1) {
+    if (first) pool_fwd_kernel<__bf16, __bf16, true><<<grid, 256, 0, st>>>(a, dp, ds);
+    else pool_fwd_kernel<float, __bf16, false><<<grid, 256, 0, st>>>(a, dp, ds);
+  } else {
+    if (first) pool_fwd_kernel<float, float, true><<<grid, 256, 0, st>>>(a, dp, ds);
+    else pool_fwd_kernel<float, float, false><<<grid, 256, 0, st>>>(a, dp, ds);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_pool_bwd(const PoolBwdArgs& a, int dtype, int64_t BH, bool first,
+                           hipStream_t st) {
+  const dim3 grid = pool_grid(a.in_rows, a.chunk, a.g.d, BH);
+  if (dtype == 1) {
+    if (first) pool_bwd_kernel<__bf16, __bf16, true><<<grid, 256, 0, st>>>(a);
+    else pool_bwd_kernel<float, __bf16, false><<<grid, 256, 0, st>>>(a);
+  } else {
+    if (first) pool_bwd_kernel<float, float, true><<<grid, 256, 0, st>>>(a);
+    else pool_bwd_kernel<float, float, false><<<grid, 256, 0, st>>>(a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace lh

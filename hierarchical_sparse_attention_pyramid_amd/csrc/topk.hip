@@ -1,0 +1,222 @@
+// Joint top-K over pyramid levels 0..L-2 (gist.science technical summary
+// §2.B; bitsgeniais post, phase 2): the K candidates first under the strict
+// order (score descending, flat index ascending), written in ascending flat
+// order.
+//
+// The pages' kernel is a chunked bitonic network built for K around 1.5K.
+// Here K reaches 32K out of 1.4M candidates per head, so the selection is an
+// exact radix select instead:
+//   1. three histogram passes over the float32 score bits (11 + 11 + 10
+//      bits; scores are non-negative, so their bit patterns order like the
+//      values) find the score T of the K-th candidate and how many
+//      candidates equal to T are still needed;
+//   2. an ordered stream compaction keeps every candidate above T and the
+//      first `need` candidates equal to T in flat order.
+// Both steps are exact integer work and give one deterministic answer.
+//
+// Workspace per head (uint32): [0] threshold prefix, [1] remaining count,
+// [2..3] unused, [4..4+2048) histogram, then four arrays of nblk block
+// counters (greater, equal, output offset, equal-before).
+#include "kernels.h"
+
+namespace lh {
+
+namespace {
+
+constexpr int kBins = 2048;
+constexpr int kSlice = 4096;  // candidates per block
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ uint32_t* head_ws(void* ws, int64_t bh, int64_t nblk) {
+  return static_cast<uint32_t*>(ws) + bh * (4 + kBins + 4 * nblk);
+}
+
+__device__ __forceinline__ void pass_bits(int pass, int& shift, int& nbits) {
+  shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+  nbits = pass == 2 ? 10 : 11;
+}
+
+__global__ __launch_bounds__(kThreads) void topk_init(void* ws, int64_t nblk, int32_t K) {
+  uint32_t* w = head_ws(ws, blockIdx.x, nblk);
+  for (int b = threadIdx.x; b < kBins; b += kThreads) w[4 + b] = 0;
+  if (threadIdx.x == 0) {
+    w[0] = 0;
+    w[1] = (uint32_t)K;
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void topk_hist(const float* score, void* ws, int64_t nblk,
+                                                      int32_t M, int32_t C, int pass) {
+  __shared__ uint32_t h[kBins];
+  const int64_t bh = blockIdx.y;
+  uint32_t* w = head_ws(ws, bh, nblk);
+  int shift, nbits;
+  pass_bits(pass, shift, nbits);
+  const uint32_t mask = (1u << nbits) - 1u;
+  const int hi = shift + nbits;
+  for (int b = threadIdx.x; b < kBins; b += kThreads) h[b] = 0;
+  __syncthreads();
+  const uint32_t prefix = w[0];
+  const float* s = score + bh * M;
+  const int i0 = blockIdx.x * kSlice;
+  const int i1 = min(i0 + kSlice, C);
+  for (int i = i0 + threadIdx.x; i < i1; i += kThreads) {
+    const uint32_t u = __float_as_uint(s[i]);
+    if (hi >= 32 || ((u ^ prefix) >> hi) == 0u) atomicAdd(&h[(u >> shift) & mask], 1u);
+  }
+  __syncthreads();
+  for (int b = threadIdx.x; b < kBins; b += kThreads)
+    if (h[b]) atomicAdd(&w[4 + b], h[b]);
+}
+
+// Exclusive prefix sum over the 256 threads of a block (in thread order).
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* sh, uint32_t& total) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  uint32_t x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) sh[wv] = x;
+  __syncthreads();
+  uint32_t before = 0;
+  total = 0;
+#pragma unroll
+  for (int k = 0; k < kThreads / 64; ++k) {
+    if (k < wv) before += sh[k];
+    total += sh[k];
+  }
+  __syncthreads();
+  return before + x - v;
+}
+
+__global__ __launch_bounds__(kThreads) void topk_pick(void* ws, int64_t nblk, int pass) {
+  __shared__ uint32_t sh[kThreads / 64];
+  uint32_t* w = head_ws(ws, blockIdx.x, nblk);
+  int shift, nbits;
+  pass_bits(pass, shift, nbits);
+  const int nb = 1 << nbits;
+  const int per = nb / kThreads;
+  const uint32_t remaining = w[1];
+  const uint32_t prefix = w[0];
+  // thread t owns bins nb-1-(t*per) down to nb-1-(t*per+per-1): descending
+  uint32_t local = 0;
+  for (int j = 0; j < per; ++j) local += w[4 + nb - 1 - (threadIdx.x * per + j)];
+  uint32_t total;
+  const uint32_t before = block_excl_scan(local, sh, total);
+  if (before < remaining && remaining <= before + local) {
+    uint32_t cum = before;
+    for (int j = 0; j < per; ++j) {
+      const int b = nb - 1 - (threadIdx.x * per + j);
+      const uint32_t c = w[4 + b];
+      if (cum + c >= remaining) {
+        w[0] = prefix | ((uint32_t)b << shift);
+        w[1] = remaining - cum;
+        break;
+      }
+      cum += c;
+    }
+  }
+  __syncthreads();
+  for (int b = threadIdx.x; b < kBins; b += kThreads) w[4 + b] = 0;
+}
+
+__global__ __launch_bounds__(kThreads) void topk_count(const float* score, void* ws, int64_t nblk,
+                                                       int32_t M, int32_t C) {
+  __shared__ uint32_t sh[kThreads / 64];
+  const int64_t bh = blockIdx.y;
+  uint32_t* w = head_ws(ws, bh, nblk);
+  const uint32_t T = w[0];
+  const float* s = score + bh * M;
+  const int i0 = blockIdx.x * kSlice;
+  const int i1 = min(i0 + kSlice, C);
+  uint32_t gt = 0, eq = 0;
+  for (int i = i0 + threadIdx.x; i < i1; i += kThreads) {
+    const uint32_t u = __float_as_uint(s[i]);
+    gt += u > T;
+    eq += u == T;
+  }
+  uint32_t tg, te;
+  block_excl_scan(gt, sh, tg);
+  block_excl_scan(eq, sh, te);
+  if (threadIdx.x == 0) {
+    uint32_t* blk = w + 4 + kBins;
+    blk[blockIdx.x] = tg;
+    blk[nblk + blockIdx.x] = te;
+  }
+}
+
+__global__ void topk_scan(void* ws, int64_t nblk) {
+  uint32_t* w = head_ws(ws, blockIdx.x, nblk);
+  if (threadIdx.x != 0) return;
+  const uint32_t need = w[1];
+  uint32_t* blk = w + 4 + kBins;
+  uint32_t off = 0, eqb = 0;
+  for (int64_t b = 0; b < nblk; ++b) {
+    const uint32_t gt = blk[b], eq = blk[nblk + b];
+    const uint32_t left = need > eqb ? need - eqb : 0u;
+    const uint32_t take = eq < left ? eq : left;
+    blk[2 * nblk + b] = off;
+    blk[3 * nblk + b] = eqb;
+    off += gt + take;
+    eqb += eq;
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void topk_write(const float* score, int32_t* sel, void* ws,
+                                                       int64_t nblk, int32_t M, int32_t C,
+                                                       int32_t K) {
+  __shared__ uint32_t sh[kThreads / 64];
+  const int64_t bh = blockIdx.y;
+  uint32_t* w = head_ws(ws, bh, nblk);
+  const uint32_t T = w[0], need = w[1];
+  const uint32_t* blk = w + 4 + kBins;
+  uint32_t off = blk[2 * nblk + blockIdx.x];
+  uint32_t eqb = blk[3 * nblk + blockIdx.x];
+  const float* s = score + bh * M;
+  int32_t* out = sel + bh * K;
+  const int i0 = blockIdx.x * kSlice;
+  const int i1 = min(i0 + kSlice, C);
+  for (int base = i0; base < i1; base += kThreads) {
+    const int i = base + threadIdx.x;
+    const bool valid = i < i1;
+    const uint32_t u = valid ? __float_as_uint(s[i]) : 0u;
+    const bool is_gt = valid && u > T;
+    const bool is_eq = valid && u == T;
+    uint32_t eq_total;
+    const uint32_t eq_before = block_excl_scan(is_eq ? 1u : 0u, sh, eq_total);
+    const bool take = is_gt || (is_eq && eqb + eq_before < need);
+    uint32_t sel_total;
+    const uint32_t sel_before = block_excl_scan(take ? 1u : 0u, sh, sel_total);
+    if (take && off + sel_before < (uint32_t)K) out[off + sel_before] = i;  // bound: never past K
+    off += sel_total;
+    eqb += eq_total;
+  }
+}
+
+}  // namespace
+
+int64_t topk_blocks(int64_t C) { return (C + kSlice - 1) / kSlice; }
+
+size_t topk_ws_bytes(int64_t BH, int64_t C) {
+  return (size_t)BH * (size_t)(4 + kBins + 4 * topk_blocks(C)) * sizeof(uint32_t);
+}
+
+hipError_t launch_topk(const float* score, int32_t* sel, void* ws, const Geo& g, int64_t BH,
+                       hipStream_t st) {
+  if (g.K == 0) return hipSuccess;
+  const int64_t nblk = topk_blocks(g.C);
+  const dim3 grid((unsigned)nblk, (unsigned)BH);
+  topk_init<<<(unsigned)BH, kThreads, 0, st>>>(ws, nblk, g.K);
+  for (int pass = 0; pass < 3; ++pass) {
+    topk_hist<<<grid, kThreads, 0, st>>>(score, ws, nblk, g.M, g.C, pass);
+    topk_pick<<<(unsigned)BH, kThreads, 0, st>>>(ws, nblk, pass);
+  }
+  topk_count<<<grid, kThreads, 0, st>>>(score, ws, nblk, g.M, g.C);
+  topk_scan<<<(unsigned)BH, 64, 0, st>>>(ws, nblk);
+  topk_write<<<grid, kThreads, 0, st>>>(score, sel, ws, nblk, g.M, g.C, g.K);
+  return hipGetLastError();
+}
+
+}  // namespace lh

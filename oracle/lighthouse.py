@@ -282,8 +282,8 @@ def forward_head(q, k, v, p: int, L: int, S: int, dtype: str):
           for name, x in (("q", q64), ("k", k64), ("v", v64))}
     qs, ks, vs = (gather_rows(lv[n], sub_idx, N, p, L) for n in ("q", "k", "v"))
     o, lse = attention(qs, ks, vs)
-    os_ = round_to(o, dtype)
-    out = round_to(scatter(to_f64(os_, dtype), pos, N, p, L), dtype)
+    os_ = round_to(o, "f64" if dtype == "f64" else "fp32")   # the layer keeps O in float32
+    out = round_to(scatter(to_f64(os_, "fp32"), pos, N, p, L), dtype)
     return dict(pq=pyr["q"], pk=pyr["k"], pv=pyr["v"], score=score, sel=sel,
                 sub_idx=sub_idx, pos=pos,
                 qs=round_to(qs, dtype), ks=round_to(ks, dtype), vs=round_to(vs, dtype),

@@ -1,0 +1,83 @@
+"""Host-only checks of the C ABI: the library loads, exports every declared
+symbol, sizes agree with the pyramid geometry, and bad arguments are rejected
+before anything is launched (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from oracle import lighthouse as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lighthouse.h")
+
+
+@pytest.fixture(scope="module")
+def lb():
+    from hierarchical_sparse_attention_pyramid_amd import binding
+    binding.load_library()
+    return binding
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:lh_status|const char\s*\*)\s*(lh_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_layer_calls():
+    names = declared_functions()
+    for n in ("lh_build_pyramid", "lh_score", "lh_topk", "lh_gather", "lh_attention",
+              "lh_scatter", "lh_forward", "lh_backward", "lh_query_sizes", "lh_last_error"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lb):
+    lib = ctypes.CDLL(lb.LIB_PATH)
+    for n in declared_functions():
+        assert hasattr(lib, n), f"{n} not exported"
+    assert set(declared_functions()) == set(lb.EXPORTS)
+
+
+@pytest.mark.parametrize("N,p,L,S", [(98304, 4, 5, 8192), (4096, 4, 3, 512), (729, 3, 4, 100),
+                                     (2048, 4, 1, 2048), (1024, 2, 9, 150)])
+def test_sizes_match_geometry(lb, N, p, L, S):
+    z = lb.lh_query_sizes(lb.make_shape(1, 16, N, 64, p, L, S, 1))
+    sizes = O.level_sizes(N, p, L)
+    assert z.M == sum(sizes) and z.n_coarse == sizes[-1]
+    assert z.C == z.M - z.n_coarse and z.K == S - z.n_coarse
+    assert z.bytes_pos == 16 * z.M * 4 and z.bytes_sub == 16 * S * 64 * 2
+    assert z.ws_forward >= z.ws_topk and z.ws_backward > 0
+
+
+@pytest.mark.parametrize("args,status", [
+    ((1, 1, 100, 64, 4, 3, 20, 1), 1),        # N not divisible by p^(L-1)
+    ((1, 1, 64, 96, 4, 3, 20, 1), 2),         # unsupported head dim
+    ((1, 1, 64, 64, 4, 3, 3, 1), 1),          # S below the coarsest level
+    ((1, 1, 64, 64, 4, 3, 85, 1), 1),         # S above M
+    ((1, 1, 64, 64, 1, 3, 20, 1), 1),         # p < 2
+    ((1, 1, 64, 64, 4, 0, 20, 1), 1),         # L < 1
+    ((1, 1, 1 << 17, 64, 2, 17, 20, 1), 2),   # too many levels
+    ((1, 1, 64, 64, 4, 3, 20, 7), 1),         # unknown dtype
+    ((0, 1, 64, 64, 4, 3, 20, 1), 1),         # empty batch
+    ((1, 4096, 1 << 20, 64, 4, 3, 1 << 16, 1), 2),  # B*H*M >= 2^31
+])
+def test_bad_shapes_are_rejected(lb, args, status):
+    with pytest.raises(lb.LighthouseError) as ei:
+        lb.lh_query_sizes(lb.Shape(*args))
+    assert ei.value.status == status
+    assert lb.load_library().lh_last_error().decode() != ""
+
+
+def test_null_pointers_and_small_workspace_are_rejected_without_a_gpu(lb):
+    lib = lb.load_library()
+    shape = lb.make_shape(1, 2, 256, 64, 4, 3, 40, 1)
+    # null q: rejected on the host, nothing launched
+    st = lib.lh_build_pyramid(ctypes.byref(shape), None, 1, 1, 1, 1, 1, 1, 1 << 20, None)
+    assert st == 1 and b"q is null" in lib.lh_last_error()
+    # workspace too small for the top-K
+    z = lb.lh_query_sizes(shape)
+    st = lib.lh_topk(ctypes.byref(shape), 1, 1, 1, z.ws_topk - 1, None)
+    assert st == 3
+    st = lib.lh_forward(ctypes.byref(shape), 1, 1, 1, 1, None, 1, z.ws_forward, None)
+    assert st == 1 and b"buffers" in lib.lh_last_error()
