@@ -1,0 +1,324 @@
+"""Benchmark of the Lighthouse attention layer on one MI355X.
+
+One step = lh_forward + lh_backward (every stage of the hot path) on one batch
+of synthetic input already resident in HBM.  The headline workload is the
+98,304-token training context (B=1, H=16, d=64, p=4, L=5, S=8192, bf16);
+`value` is its whole-job throughput in tokens/s.  Alongside:
+  * per-stage times from HIP events on the launch stream and each stage's
+    fraction of its HBM or matrix-core roofline;
+  * the 524,288-token layer (H=16, d=128, p=4, L=6, S=16384) forward and
+    forward+backward, against the same-GPU dense causal attention (the same
+    attention kernels at S = N);
+  * the CPU oracle timed on one head of the headline workload (cpu_baseline).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-long] [--no-cpu]
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0      # dense MFMA bf16
+PEAK_FP32_TFLOPS = 157.3
+METRIC = "Lighthouse layer tokens/s fwd+bwd at N=98K/512K; speedup vs dense causal attn"
+HEADLINE = "train_n98k_bf16"
+LONG = "long_n512k_bf16"
+KERNEL_OF_STAGE = {
+    "attention_fwd": ("attn_fwd_bf16", "attention_bf16.hip"),
+    "attention_dkdv": ("attn_bwd_dkdv_bf16", "attention_bf16.hip"),
+    "attention_dq": ("attn_bwd_dq_bf16", "attention_bf16.hip"),
+    "scatter": ("bcast_kernel", "scatter.hip"),
+    "gather_bwd": ("bcast_kernel", "scatter.hip"),
+    "scatter_bwd": ("pool_bwd_kernel", "pyramid.hip"),
+    "pyramid_score": ("pool_fwd_kernel", "pyramid.hip"),
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def causal_pairs(S):
+    return S * (S + 1) / 2.0
+
+
+def stage_work(cfg, z):
+    """Algorithmic HBM bytes or matrix flops of each stage for all B*H heads.
+
+    Bytes count what a stage must read and write once (inputs, outputs), not
+    implementation traffic such as the float32 partial sums of deep pyramids.
+    Attention flops count causal (i, j <= i) pairs: forward 2 matmuls, the
+    backward 5 (recompute of QK^T, dP, dV, dK, dQ), split as 4 in the
+    key-block pass and 1 (dQ) in the query-block pass; the query-block pass
+    also recomputes QK^T and dP, which is not counted."""
+    BH = cfg.B * cfg.H
+    N, d, S, M = cfg.N, cfg.d, cfg.S, z.M
+    e = 2 if cfg.dtype == "bf16" else 4
+    C, K = z.C, z.K
+    pairs = causal_pairs(S)
+    return {
+        "pyramid_score": ("hbm", BH * (3 * N * d * e + 3 * (M - N) * d * e + 4 * M)),
+        "topk": ("hbm", BH * (4 * C + 4 * K)),
+        "gather": ("hbm", BH * (2 * 3 * S * d * e + 4 * K + 4 * S + 4 * M)),
+        "attention_fwd": ("mfma", BH * 4 * d * pairs),
+        "scatter": ("hbm", BH * (4 * S * d + 4 * M + N * d * e)),
+        "scatter_bwd": ("hbm", BH * (N * d * e + 4 * M + S * d * e)),
+        "attention_delta": ("hbm", BH * (4 * S * d + S * d * e + 4 * S)),
+        "attention_dkdv": ("mfma", BH * 8 * d * pairs),
+        "attention_dq": ("mfma", BH * 2 * d * pairs),
+        "gather_bwd": ("hbm", BH * (3 * 4 * S * d + 4 * M + 3 * N * d * e)),
+    }
+
+
+def roofline_entry(kind, work, ms, dtype):
+    if kind == "hbm":
+        achieved = work / (ms * 1e-3) / 1e9
+        peak, unit = PEAK_HBM_GBS, "GB/s"
+    else:
+        achieved = work / (ms * 1e-3) / 1e12
+        peak = PEAK_BF16_TFLOPS if dtype == "bf16" else PEAK_FP32_TFLOPS
+        unit = "TFLOP/s"
+    return {"bound": kind, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4)}
+
+
+def src_hash(fname):
+    path = os.path.join(ROOT, "hierarchical_sparse_attention_pyramid_amd", "csrc", fname)
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel, fname):
+    """HBM bytes per launch from the committed rocprofv3 --pmc summary, if it
+    was taken on the current source of that kernel; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path)).get(kernel)
+    if not rec or rec.get("source_sha256_16") != src_hash(fname):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+class Layer:
+    """Device tensors of one workload (inputs from the seeded generator)."""
+
+    def __init__(self, cfg, torch, lb, backward=True):
+        from synth import inputs as synth
+        t0 = time.time()
+        names = ("q", "k", "v", "dout") if backward else ("q", "k", "v")
+        host = synth.make_inputs(cfg, tensors=names)
+        log(f"[bench] {cfg.name}: inputs drawn in {time.time() - t0:.1f}s")
+        self.cfg = cfg
+        self.x = {}
+        for n in names:
+            a = host.pop(n)
+            t = torch.from_numpy(a.view("int16")).view(torch.bfloat16) if cfg.dtype == "bf16" \
+                else torch.from_numpy(a)
+            self.x[n] = t.cuda()
+            del a, t
+        self.shape = lb.make_shape(cfg.B, cfg.H, cfg.N, cfg.d, cfg.p, cfg.L, cfg.S,
+                                   self.x["q"].dtype)
+        self.bufs = lb.LayerBuffers(self.shape)
+        z = self.bufs.sizes
+        self.z = z
+        self.out = torch.empty_like(self.x["q"])
+        if backward:
+            self.dq, self.dk, self.dv = (torch.empty_like(self.x["q"]) for _ in range(3))
+        self.ws = lb.workspace(max(z.ws_forward, z.ws_backward))
+        self.lb = lb
+
+    def forward(self):
+        x = self.x
+        self.lb.lh_forward(self.shape, x["q"], x["k"], x["v"], self.out, self.bufs, self.ws)
+
+    def step(self):
+        self.forward()
+        self.lb.lh_backward(self.shape, self.x["dout"], self.bufs, self.dq, self.dk, self.dv,
+                            self.ws)
+
+    def profile(self):
+        x = self.x
+        return self.lb.lh_profile_step(self.shape, x["q"], x["k"], x["v"], self.out, self.bufs,
+                                       x["dout"], self.dq, self.dk, self.dv, self.ws)
+
+
+def time_fn(torch, fn, steps, warmup):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps
+
+
+def calibration_copy(torch):
+    """A plain 256 MiB device copy, so that HBM counters of a --pmc run can be
+    scaled against a kernel of known traffic (256 MiB read + 256 MiB write)."""
+    a = torch.ones(64 << 20, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+
+
+def dense_times(torch, lb, lay, steps, warmup):
+    """Same-GPU dense causal attention on the full N (forward, forward+backward)."""
+    cfg = lay.cfg
+    BH, N, d = cfg.B * cfg.H, cfg.N, cfg.d
+    shape = lb.make_shape(cfg.B, cfg.H, N, d, cfg.p, 1, N, lay.x["q"].dtype)
+    o = torch.empty(cfg.B, cfg.H, N, d, dtype=torch.float32, device="cuda")
+    lse = torch.empty(cfg.B, cfg.H, N, dtype=torch.float32, device="cuda")
+    q, k, v, g = lay.x["q"], lay.x["k"], lay.x["v"], lay.x["dout"]
+
+    def fwd():
+        lb.lh_attention(shape, q, k, v, o, lse)
+
+    t_f = time_fn(torch, fwd, steps, warmup)
+    log(f"[bench] dense N={N}: forward {t_f:.1f} ms")
+    dq, dk, dv = (torch.empty(cfg.B, cfg.H, N, d, dtype=torch.float32, device="cuda")
+                  for _ in range(3))
+    ws = lb.workspace(lb.lh_query_sizes(shape).ws_attention_backward)
+
+    def fb():
+        fwd()
+        lb.lh_attention_backward(shape, q, k, v, o, lse, g, dq, dk, dv, ws)
+
+    t_fb = time_fn(torch, fb, steps, 0)
+    log(f"[bench] dense N={N}: forward+backward {t_fb:.1f} ms")
+    flops_f = BH * 4 * d * causal_pairs(N)
+    del o, lse, dq, dk, dv, ws
+    torch.cuda.empty_cache()
+    return t_f, t_fb, flops_f
+
+
+def cpu_baseline(cfg):
+    """The oracle as it stands, on one head of the headline workload, scaled to
+    the whole layer (all B*H heads)."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import lighthouse as O
+    from synth import inputs as synth
+    x = synth.make_inputs(cfg, tensors=("q", "k", "v", "dout"), heads=[(0, 0)])
+    t0 = time.perf_counter()
+    f = O.forward_head(x["q"][0], x["k"][0], x["v"][0], cfg.p, cfg.L, cfg.S, cfg.dtype)
+    O.backward_head(x["dout"][0], f, cfg.p, cfg.L, cfg.dtype)
+    t = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    heads = cfg.B * cfg.H
+    return {"value": round(cfg.B * cfg.N / (t * heads), 2), "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"head (b=0,h=0) of {cfg.name}, forward+backward, {t:.2f}s; "
+                      f"layer time = {heads} x head time; {os.cpu_count()} host cpus visible"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--profile-reps", type=int, default=5)
+    ap.add_argument("--dense-steps", type=int, default=2)
+    ap.add_argument("--no-long", action="store_true", help="skip the 512K comparison")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the layer is not sharded across GPUs)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from hierarchical_sparse_attention_pyramid_amd import binding as lb
+    from synth import inputs as synth
+    lb.load_library()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    calibration_copy(torch)
+
+    cfg = synth.CONFIGS[HEADLINE]
+    lay = Layer(cfg, torch, lb)
+    ms = time_fn(torch, lay.step, args.steps, args.warmup)
+    tokens = cfg.B * cfg.N
+    log(f"[bench] {cfg.name}: {ms:.3f} ms per forward+backward step")
+    ms_fwd = time_fn(torch, lay.forward, args.steps, 2)
+    prof = [lay.profile() for _ in range(args.profile_reps)]
+    stages_ms = {k: sorted(p[k] for p in prof)[len(prof) // 2] for k in prof[0]}
+    work = stage_work(cfg, lay.z)
+    stages = {}
+    for k, t in stages_ms.items():
+        kind, w = work[k]
+        stages[k] = {"ms": round(t, 4), **roofline_entry(kind, w, t, cfg.dtype)}
+    dom = max((k for k in stages_ms if k in KERNEL_OF_STAGE), key=lambda k: stages_ms[k])
+    kname, kfile = KERNEL_OF_STAGE[dom]
+    kind, w = work[dom]
+    roof = roofline_entry(kind, w, stages_ms[dom], cfg.dtype)
+    roof["kernel"] = kname
+    roof["traffic"] = measured_traffic(kname, kfile)
+    log(f"[bench] stages (ms): " + ", ".join(f"{k}={v:.4f}" for k, v in stages_ms.items()))
+    del lay
+    torch.cuda.empty_cache()
+
+    long_ctx = None
+    if not args.no_long:
+        lcfg = synth.CONFIGS[LONG]
+        ll = Layer(lcfg, torch, lb)
+        l_fb = time_fn(torch, ll.step, max(3, args.steps // 4), 2)
+        l_f = time_fn(torch, ll.forward, max(3, args.steps // 4), 1)
+        lprof = ll.profile()
+        log(f"[bench] {lcfg.name}: forward {l_f:.2f} ms, forward+backward {l_fb:.2f} ms")
+        d_f, d_fb, d_flops = dense_times(torch, lb, ll, args.dense_steps, 1)
+        long_ctx = {
+            "workload": lcfg.name, "N": lcfg.N, "H": lcfg.H, "d": lcfg.d, "L": lcfg.L,
+            "S": lcfg.S,
+            "lighthouse_fwd_ms": round(l_f, 3), "lighthouse_fwdbwd_ms": round(l_fb, 3),
+            "lighthouse_fwdbwd_tokens_per_s": round(lcfg.B * lcfg.N / (l_fb * 1e-3), 1),
+            "lighthouse_stage_ms": {k: round(v, 4) for k, v in lprof.items()},
+            "dense_fwd_ms": round(d_f, 2), "dense_fwdbwd_ms": round(d_fb, 2),
+            "dense_fwd_tflops": round(d_flops / (d_f * 1e-3) / 1e12, 1),
+            "speedup_fwd": round(d_f / l_f, 2), "speedup_fwdbwd": round(d_fb / l_fb, 2),
+        }
+        del ll
+        torch.cuda.empty_cache()
+
+    cpu = None if args.no_cpu else cpu_baseline(cfg)
+    if cpu:
+        log(f"[bench] cpu oracle: {cpu['value']} tokens/s ({cpu['sample']})")
+
+    rec = {
+        "metric": METRIC,
+        "value": round(tokens / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "B": cfg.B, "H": cfg.H, "N": cfg.N, "d": cfg.d,
+                   "p": cfg.p, "L": cfg.L, "S": cfg.S, "pass": "forward+backward",
+                   "forward_only_ms": round(ms_fwd, 4)},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "stages": stages,
+        "long_context": long_ctx,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

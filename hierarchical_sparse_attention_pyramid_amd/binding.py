@@ -48,7 +48,11 @@ class Buffers(ctypes.Structure):
 
 EXPORTS = ["lh_query_sizes", "lh_last_error", "lh_build_pyramid", "lh_score", "lh_topk",
            "lh_gather", "lh_attention", "lh_scatter", "lh_forward", "lh_scatter_backward",
-           "lh_attention_backward", "lh_gather_backward", "lh_backward"]
+           "lh_attention_backward", "lh_gather_backward", "lh_backward", "lh_profile_step"]
+
+PROFILE_STAGES = ["pyramid_score", "topk", "gather", "attention_fwd", "scatter",
+                  "scatter_bwd", "attention_delta", "attention_dkdv", "attention_dq",
+                  "gather_bwd"]
 
 _lib = None
 
@@ -77,6 +81,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "lh_attention_backward": [sp, P, P, P, P, P, P, P, P, P, P, S, P],
         "lh_gather_backward": [sp, P, P, P, P, P, P, P, P],
         "lh_backward": [sp, P, ctypes.POINTER(Buffers), P, P, P, P, S, P],
+        "lh_profile_step": [sp, P, P, P, P, ctypes.POINTER(Buffers), P, P, P, P, P, S,
+                            ctypes.POINTER(ctypes.c_float), P],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -186,6 +192,18 @@ def lh_backward(shape, dout, bufs: "LayerBuffers", dq, dk, dv, ws, stream=None):
     _check(load_library().lh_backward(ctypes.byref(shape), _ptr(dout), ctypes.byref(cb),
                                       _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), _nbytes(ws),
                                       _stream(stream)))
+
+
+def lh_profile_step(shape, q, k, v, out, bufs: "LayerBuffers", dout, dq, dk, dv, ws,
+                    stream=None) -> dict:
+    """Per-stage milliseconds of one forward + backward (waits for the stream)."""
+    cb = bufs.as_ctypes()
+    ms = (ctypes.c_float * len(PROFILE_STAGES))()
+    _check(load_library().lh_profile_step(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v),
+                                          _ptr(out), ctypes.byref(cb), _ptr(dout), _ptr(dq),
+                                          _ptr(dk), _ptr(dv), _ptr(ws), _nbytes(ws), ms,
+                                          _stream(stream)))
+    return dict(zip(PROFILE_STAGES, list(ms)))
 
 
 # ------------------------------------------------------------- allocation helpers

@@ -454,7 +454,8 @@ hipError_t launch_attn_fwd_f32(const float* q, const float* k, const float* v, f
                                int64_t S, int d, int64_t BH, hipStream_t st);
 hipError_t launch_attn_bwd_f32(const float* q, const float* k, const float* v, const float* lse,
                                const float* delta, const float* dout, float* dq, float* dk,
-                               float* dv, int64_t S, int d, int64_t BH, hipStream_t st);
+                               float* dv, int64_t S, int d, int64_t BH, hipStream_t st,
+                               hipEvent_t* ev);
 
 hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, float* o, float* lse,
                            int64_t S, int d, int dtype, int64_t BH, hipStream_t st) {
@@ -479,20 +480,23 @@ hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, float* o
 hipError_t launch_attn_bwd(const void* q, const void* k, const void* v, const float* o,
                            const float* lse, const void* dout, float* dq, float* dk, float* dv,
                            float* delta, int64_t S, int d, int dtype, int64_t BH,
-                           hipStream_t st) {
+                           hipStream_t st, hipEvent_t* ev) {
   if (S == 0) return hipSuccess;
   const int64_t rows = S * BH;
   const int rgs = 256 / (d / 8);
   const unsigned dgrid = (unsigned)((rows + rgs - 1) / rgs);
-  if (dtype == 0) {
-    attn_delta<float><<<dgrid, 256, 0, st>>>(o, static_cast<const float*>(dout), delta, rows, d);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    return launch_attn_bwd_f32(static_cast<const float*>(q), static_cast<const float*>(k),
-                               static_cast<const float*>(v), lse, delta,
-                               static_cast<const float*>(dout), dq, dk, dv, S, d, BH, st);
+  const bool f32 = dtype == 0;
+  if (f32) attn_delta<float><<<dgrid, 256, 0, st>>>(o, static_cast<const float*>(dout), delta, rows, d);
+  else attn_delta<__bf16><<<dgrid, 256, 0, st>>>(o, static_cast<const __bf16*>(dout), delta, rows, d);
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess && ev) e = hipEventRecord(ev[0], st);
+  if (e != hipSuccess) return e;
+  if (f32) {
+    e = launch_attn_bwd_f32(static_cast<const float*>(q), static_cast<const float*>(k),
+                            static_cast<const float*>(v), lse, delta,
+                            static_cast<const float*>(dout), dq, dk, dv, S, d, BH, st, ev);
+    return e;
   }
-  attn_delta<__bf16><<<dgrid, 256, 0, st>>>(o, static_cast<const __bf16*>(dout), delta, rows, d);
   const float scale = 1.0f / sqrtf((float)d);
   const float sl2 = kLog2e * scale;
   const auto Q = static_cast<const __bf16*>(q);
@@ -502,15 +506,23 @@ hipError_t launch_attn_bwd(const void* q, const void* k, const void* v, const fl
   if (d == 64) {
     const dim3 g1((unsigned)((S + BwdKVCfg<64>::kKB - 1) / BwdKVCfg<64>::kKB), (unsigned)BH);
     attn_bwd_dkdv_bf16<64><<<g1, 256, 0, st>>>(Q, K, V, G, lse, delta, dk, dv, (int)S, sl2, scale);
-    const dim3 g2((unsigned)((S + BwdQCfg<64>::kQB - 1) / BwdQCfg<64>::kQB), (unsigned)BH);
-    attn_bwd_dq_bf16<64><<<g2, 256, 0, st>>>(Q, K, V, G, lse, delta, dq, (int)S, sl2, scale);
   } else {
     const dim3 g1((unsigned)((S + BwdKVCfg<128>::kKB - 1) / BwdKVCfg<128>::kKB), (unsigned)BH);
     attn_bwd_dkdv_bf16<128><<<g1, 256, 0, st>>>(Q, K, V, G, lse, delta, dk, dv, (int)S, sl2, scale);
+  }
+  e = hipGetLastError();
+  if (e == hipSuccess && ev) e = hipEventRecord(ev[1], st);
+  if (e != hipSuccess) return e;
+  if (d == 64) {
+    const dim3 g2((unsigned)((S + BwdQCfg<64>::kQB - 1) / BwdQCfg<64>::kQB), (unsigned)BH);
+    attn_bwd_dq_bf16<64><<<g2, 256, 0, st>>>(Q, K, V, G, lse, delta, dq, (int)S, sl2, scale);
+  } else {
     const dim3 g2((unsigned)((S + BwdQCfg<128>::kQB - 1) / BwdQCfg<128>::kQB), (unsigned)BH);
     attn_bwd_dq_bf16<128><<<g2, 256, 0, st>>>(Q, K, V, G, lse, delta, dq, (int)S, sl2, scale);
   }
-  return hipGetLastError();
+  e = hipGetLastError();
+  if (e == hipSuccess && ev) e = hipEventRecord(ev[2], st);
+  return e;
 }
 
 }  // namespace lh

@@ -174,17 +174,20 @@ hipError_t launch_attn_fwd_f32(const float* q, const float* k, const float* v, f
 
 hipError_t launch_attn_bwd_f32(const float* q, const float* k, const float* v, const float* lse,
                                const float* delta, const float* dout, float* dq, float* dk,
-                               float* dv, int64_t S, int d, int64_t BH, hipStream_t st) {
+                               float* dv, int64_t S, int d, int64_t BH, hipStream_t st,
+                               hipEvent_t* ev) {
   const dim3 grid((unsigned)((S + kRows - 1) / kRows), (unsigned)BH);
   const float scale = 1.0f / sqrtf((float)d);
-  if (d == 64) {
-    attn_bwd_dkdv_f32<64><<<grid, 256, 0, st>>>(q, k, v, dout, lse, delta, dk, dv, (int)S, scale);
-    attn_bwd_dq_f32<64><<<grid, 256, 0, st>>>(q, k, v, dout, lse, delta, dq, (int)S, scale);
-  } else {
-    attn_bwd_dkdv_f32<128><<<grid, 256, 0, st>>>(q, k, v, dout, lse, delta, dk, dv, (int)S, scale);
-    attn_bwd_dq_f32<128><<<grid, 256, 0, st>>>(q, k, v, dout, lse, delta, dq, (int)S, scale);
-  }
-  return hipGetLastError();
+  if (d == 64) attn_bwd_dkdv_f32<64><<<grid, 256, 0, st>>>(q, k, v, dout, lse, delta, dk, dv, (int)S, scale);
+  else attn_bwd_dkdv_f32<128><<<grid, 256, 0, st>>>(q, k, v, dout, lse, delta, dk, dv, (int)S, scale);
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess && ev) e = hipEventRecord(ev[1], st);
+  if (e != hipSuccess) return e;
+  if (d == 64) attn_bwd_dq_f32<64><<<grid, 256, 0, st>>>(q, k, v, dout, lse, delta, dq, (int)S, scale);
+  else attn_bwd_dq_f32<128><<<grid, 256, 0, st>>>(q, k, v, dout, lse, delta, dq, (int)S, scale);
+  e = hipGetLastError();
+  if (e == hipSuccess && ev) e = hipEventRecord(ev[2], st);
+  return e;
 }
 
 }  // namespace lh

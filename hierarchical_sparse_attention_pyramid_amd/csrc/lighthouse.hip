@@ -336,11 +336,8 @@ lh_status lh_scatter(const lh_shape* shape, const float* os, const int32_t* pos,
   return LH_OK;
 }
 
-lh_status lh_forward(const lh_shape* shape, const void* q, const void* k, const void* v,
-                     void* out, const lh_buffers* b, void* ws, size_t ws_bytes, void* stream) {
-  Plan P;
-  lh_status s = make_plan(shape, P);
-  if (s != LH_OK) return s;
+static lh_status check_forward_args(const Plan& P, const void* q, const void* k, const void* v,
+                                    void* out, const lh_buffers* b) {
   LH_NEED(b, "buffers");
   LH_NEED(q, "q");
   LH_NEED(k, "k");
@@ -360,18 +357,28 @@ lh_status lh_forward(const lh_shape* shape, const void* q, const void* k, const 
   LH_NEED(b->vs, "buffers.vs");
   LH_NEED(b->os, "buffers.os");
   LH_NEED(b->lse, "buffers.lse");
-  if ((s = check_ws(ws, ws_bytes, P.sz.ws_forward)) != LH_OK) return s;
-  const hipStream_t st = static_cast<hipStream_t>(stream);
+  return LH_OK;
+}
+
+// Forward launch sequence; when `ev` is given, ev[i] is recorded after stage i
+// (pyramid+score, top-K, gather, attention, scatter).
+static lh_status run_forward(const Plan& P, const void* q, const void* k, const void* v, void* out,
+                             const lh_buffers* b, void* ws, hipStream_t st, hipEvent_t* ev) {
+  lh_status s;
   if ((s = run_pool(P, q, k, v, b->pq, b->pk, b->pv, b->score, ws, P.g.L > 1, true, st)) != LH_OK)
     return s;
+  if (ev) LH_HIP(hipEventRecord(ev[0], st), "event");
   LH_HIP(lh::launch_topk(b->score, b->sel, ws, P.g, P.BH, st), "topk");
+  if (ev) LH_HIP(hipEventRecord(ev[1], st), "event");
   const void* lv0[3] = {q, k, v};
   const void* pyr[3] = {b->pq, b->pk, b->pv};
   void* sub[3] = {b->qs, b->ks, b->vs};
   LH_HIP(lh::launch_gather(b->sel, lv0, pyr, b->sub_idx, b->pos, sub, P.g, P.dtype, P.BH, st),
          "gather");
+  if (ev) LH_HIP(hipEventRecord(ev[2], st), "event");
   LH_HIP(lh::launch_attn_fwd(b->qs, b->ks, b->vs, b->os, b->lse, P.g.S, P.g.d, P.dtype, P.BH, st),
          "attention");
+  if (ev) LH_HIP(hipEventRecord(ev[3], st), "event");
   lh::BcastArgs a{};
   a.src[0] = b->os;
   a.out[0] = out;
@@ -379,7 +386,18 @@ lh_status lh_forward(const lh_shape* shape, const void* q, const void* k, const 
   a.mean = 1;
   a.g = P.g;
   LH_HIP(lh::launch_bcast(a, P.dtype, 1, P.BH, st), "scatter");
+  if (ev) LH_HIP(hipEventRecord(ev[4], st), "event");
   return LH_OK;
+}
+
+lh_status lh_forward(const lh_shape* shape, const void* q, const void* k, const void* v,
+                     void* out, const lh_buffers* b, void* ws, size_t ws_bytes, void* stream) {
+  Plan P;
+  lh_status s = make_plan(shape, P);
+  if (s != LH_OK) return s;
+  if ((s = check_forward_args(P, q, k, v, out, b)) != LH_OK) return s;
+  if ((s = check_ws(ws, ws_bytes, P.sz.ws_forward)) != LH_OK) return s;
+  return run_forward(P, q, k, v, out, b, ws, static_cast<hipStream_t>(stream), nullptr);
 }
 
 static lh_status run_scatter_bwd(const Plan& P, const void* dout, const int32_t* pos, void* dos,
@@ -432,7 +450,8 @@ lh_status lh_attention_backward(const lh_shape* shape, const void* qs, const voi
   LH_NEED(dvs, "dvs");
   if ((s = check_ws(ws, ws_bytes, P.sz.ws_attention_backward)) != LH_OK) return s;
   LH_HIP(lh::launch_attn_bwd(qs, ks, vs, os, lse, dos, dqs, dks, dvs, static_cast<float*>(ws),
-                             P.g.S, P.g.d, P.dtype, P.BH, static_cast<hipStream_t>(stream)),
+                             P.g.S, P.g.d, P.dtype, P.BH, static_cast<hipStream_t>(stream),
+                             nullptr),
          "attention_backward");
   return LH_OK;
 }
@@ -465,11 +484,8 @@ lh_status lh_gather_backward(const lh_shape* shape, const float* dqs, const floa
   return LH_OK;
 }
 
-lh_status lh_backward(const lh_shape* shape, const void* dout, const lh_buffers* b, void* dq,
-                      void* dk, void* dv, void* ws, size_t ws_bytes, void* stream) {
-  Plan P;
-  lh_status s = make_plan(shape, P);
-  if (s != LH_OK) return s;
+static lh_status check_backward_args(const void* dout, const lh_buffers* b, void* dq, void* dk,
+                                     void* dv) {
   LH_NEED(b, "buffers");
   LH_NEED(dout, "dout");
   LH_NEED(b->pos, "buffers.pos");
@@ -481,8 +497,13 @@ lh_status lh_backward(const lh_shape* shape, const void* dout, const lh_buffers*
   LH_NEED(dq, "dq");
   LH_NEED(dk, "dk");
   LH_NEED(dv, "dv");
-  if ((s = check_ws(ws, ws_bytes, P.sz.ws_backward)) != LH_OK) return s;
-  const hipStream_t st = static_cast<hipStream_t>(stream);
+  return LH_OK;
+}
+
+// Backward launch sequence; when `ev` is given, ev[i] is recorded after stage
+// i (scatter backward, delta, dK/dV pass, dQ pass, gather backward).
+static lh_status run_backward(const Plan& P, const void* dout, const lh_buffers* b, void* dq,
+                              void* dk, void* dv, void* ws, hipStream_t st, hipEvent_t* ev) {
   char* w = static_cast<char*>(ws);
   void* dos = w;
   w += align_up(P.sz.bytes_sub);
@@ -494,9 +515,11 @@ lh_status lh_backward(const lh_shape* shape, const void* dout, const lh_buffers*
   w += align_up(P.sz.bytes_sub_f32);
   float* delta = reinterpret_cast<float*>(w);
   w += align_up(P.sz.bytes_lse);
+  lh_status s;
   if ((s = run_scatter_bwd(P, dout, b->pos, dos, w, st)) != LH_OK) return s;
+  if (ev) LH_HIP(hipEventRecord(ev[0], st), "event");
   LH_HIP(lh::launch_attn_bwd(b->qs, b->ks, b->vs, b->os, b->lse, dos, dqs, dks, dvs, delta, P.g.S,
-                             P.g.d, P.dtype, P.BH, st),
+                             P.g.d, P.dtype, P.BH, st, ev ? ev + 1 : nullptr),
          "attention_backward");
   lh::BcastArgs a{};
   a.src[0] = dqs;
@@ -509,7 +532,49 @@ lh_status lh_backward(const lh_shape* shape, const void* dout, const lh_buffers*
   a.mean = 0;
   a.g = P.g;
   LH_HIP(lh::launch_bcast(a, P.dtype, 3, P.BH, st), "gather_backward");
+  if (ev) LH_HIP(hipEventRecord(ev[4], st), "event");
   return LH_OK;
+}
+
+lh_status lh_backward(const lh_shape* shape, const void* dout, const lh_buffers* b, void* dq,
+                      void* dk, void* dv, void* ws, size_t ws_bytes, void* stream) {
+  Plan P;
+  lh_status s = make_plan(shape, P);
+  if (s != LH_OK) return s;
+  if ((s = check_backward_args(dout, b, dq, dk, dv)) != LH_OK) return s;
+  if ((s = check_ws(ws, ws_bytes, P.sz.ws_backward)) != LH_OK) return s;
+  return run_backward(P, dout, b, dq, dk, dv, ws, static_cast<hipStream_t>(stream), nullptr);
+}
+
+lh_status lh_profile_step(const lh_shape* shape, const void* q, const void* k, const void* v,
+                          void* out, const lh_buffers* b, const void* dout, void* dq, void* dk,
+                          void* dv, void* ws, size_t ws_bytes, float* ms, void* stream) {
+  Plan P;
+  lh_status s = make_plan(shape, P);
+  if (s != LH_OK) return s;
+  LH_NEED(ms, "ms");
+  if ((s = check_forward_args(P, q, k, v, out, b)) != LH_OK) return s;
+  if ((s = check_backward_args(dout, b, dq, dk, dv)) != LH_OK) return s;
+  if ((s = check_ws(ws, ws_bytes, std::max(P.sz.ws_forward, P.sz.ws_backward))) != LH_OK) return s;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  hipEvent_t ev[LH_PROFILE_STAGES + 1];
+  int made = 0;
+  for (; made <= LH_PROFILE_STAGES; ++made) {
+    const hipError_t e = hipEventCreate(&ev[made]);
+    if (e != hipSuccess) {
+      for (int i = 0; i < made; ++i) hipEventDestroy(ev[i]);
+      return hip_fail(e, "hipEventCreate");
+    }
+  }
+  hipError_t e = hipEventRecord(ev[0], st);
+  if (e == hipSuccess) s = run_forward(P, q, k, v, out, b, ws, st, ev + 1);
+  if (e == hipSuccess && s == LH_OK) s = run_backward(P, dout, b, dq, dk, dv, ws, st, ev + 6);
+  if (e == hipSuccess && s == LH_OK) e = hipEventSynchronize(ev[LH_PROFILE_STAGES]);
+  for (int i = 0; e == hipSuccess && s == LH_OK && i < LH_PROFILE_STAGES; ++i)
+    e = hipEventElapsedTime(&ms[i], ev[i], ev[i + 1]);
+  for (int i = 0; i <= LH_PROFILE_STAGES; ++i) hipEventDestroy(ev[i]);
+  if (e != hipSuccess) return hip_fail(e, "profile");
+  return s;
 }
 
 }  // extern "C"

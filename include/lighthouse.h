@@ -193,6 +193,20 @@ lh_status lh_backward(const lh_shape *shape, const void *dout, const lh_buffers 
                       void *dq, void *dk, void *dv, void *ws, size_t ws_bytes,
                       void *stream);
 
+/* Measurement aid (not part of the layer's computation): runs lh_forward and
+ * then lh_backward once on `stream`, records a hipEvent after each stage and
+ * writes the elapsed milliseconds of each stage to ms[0..LH_PROFILE_STAGES-1]:
+ *   0 pyramid + scores   1 top-K            2 gather        3 attention
+ *   4 scatter            5 scatter backward 6 rowsum(dO*O)  7 attention dK,dV
+ *   8 attention dQ       9 gather+pool backward
+ * Arguments as for lh_forward / lh_backward; ws must hold
+ * max(ws_forward, ws_backward) bytes.  Unlike every other entry point this
+ * call waits for the stream before returning. */
+#define LH_PROFILE_STAGES 10
+lh_status lh_profile_step(const lh_shape *shape, const void *q, const void *k, const void *v,
+                          void *out, const lh_buffers *bufs, const void *dout, void *dq, void *dk,
+                          void *dv, void *ws, size_t ws_bytes, float *ms, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

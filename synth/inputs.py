@@ -19,7 +19,8 @@ from __future__ import annotations
 
 import dataclasses
 import os
-from concurrent.futures import ThreadPoolExecutor
+import multiprocessing
+from concurrent.futures import ProcessPoolExecutor
 
 import numpy as np
 
@@ -59,9 +60,13 @@ CONFIGS = {
 def bf16_bits_from_f32(x: np.ndarray) -> np.ndarray:
     """Round float32 values to bfloat16 (nearest, ties to even); return uint16 bits."""
     u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
-    nan = (u & 0x7FFFFFFF) > 0x7F800000
-    r = (u + (np.uint32(0x7FFF) + ((u >> 16) & 1))) >> 16
-    r = np.where(nan, (u >> 16) | 0x40, r)
+    r = (u >> 16) & np.uint32(1)
+    r += np.uint32(0x7FFF)
+    r += u
+    r >>= 16
+    nan = (u & np.uint32(0x7FFFFFFF)) > np.uint32(0x7F800000)
+    if nan.any():
+        r[nan] = (u[nan] >> 16) | 0x40
     return r.astype(np.uint16)
 
 
@@ -101,21 +106,27 @@ def _head_storage(args):
 
 
 def make_inputs(cfg: Config, tensors=("q", "k", "v"), heads=None, N=None,
-                threads: int | None = None) -> dict:
+                workers: int | None = None) -> dict:
     """Storage-typed arrays [B, H', N, d] (uint16 bf16 bits or float32).
 
     ``heads`` restricts the draw to a list of (b, h) pairs (the result then has
-    shape [len(heads), N, d]); ``N`` overrides the config's length.
+    shape [len(heads), N, d]); ``N`` overrides the config's length.  Large
+    draws are spread over worker processes (one job per head and tensor); the
+    values do not depend on how the work is split.
     """
     N = cfg.N if N is None else N
     pairs = [(b, h) for b in range(cfg.B) for h in range(cfg.H)] if heads is None else list(heads)
-    threads = threads or min(16, os.cpu_count() or 1)
-    out = {}
-    for t in tensors:
-        jobs = [(cfg.seed, t, b, h, N, cfg.d, cfg.planted and t != "dout", cfg.dtype)
-                for (b, h) in pairs]
-        with ThreadPoolExecutor(threads) as ex:
+    jobs = [(cfg.seed, t, b, h, N, cfg.d, cfg.planted and t != "dout", cfg.dtype)
+            for t in tensors for (b, h) in pairs]
+    workers = workers or min(16, os.cpu_count() or 1)
+    if len(jobs) > 1 and N * cfg.d >= (1 << 22) and workers > 1:
+        ctx = multiprocessing.get_context("spawn")
+        with ProcessPoolExecutor(min(workers, len(jobs)), mp_context=ctx) as ex:
             parts = list(ex.map(_head_storage, jobs))
-        arr = np.stack(parts)
+    else:
+        parts = [_head_storage(j) for j in jobs]
+    out = {}
+    for i, t in enumerate(tensors):
+        arr = np.stack(parts[i * len(pairs):(i + 1) * len(pairs)])
         out[t] = arr.reshape(cfg.B, cfg.H, N, cfg.d) if heads is None else arr
     return out
