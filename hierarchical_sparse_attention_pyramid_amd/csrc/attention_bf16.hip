@@ -22,6 +22,30 @@
 // log-sum-exp.
 #include "kernels.h"
 
+// Forward tiling (queries per wave, waves per workgroup, minimum waves per
+// SIMD the register budget must allow).
+#ifndef LH_FWD64_QW
+#define LH_FWD64_QW 32
+#define LH_FWD64_WAVES 4
+#define LH_FWD64_MINW 2
+#endif
+#ifndef LH_FWD128_QW
+#define LH_FWD128_QW 32
+#define LH_FWD128_WAVES 8
+#define LH_FWD128_MINW 2
+#endif
+// Backward: waves per workgroup of the key-block (dK, dV) and query-block
+// (dQ) passes; every wave owns 32 keys or 32 queries.
+#ifndef LH_BKV64_WAVES
+#define LH_BKV64_WAVES 4
+#define LH_BKV64_MINW 2
+#define LH_BKV128_WAVES 8
+#define LH_BKV128_MINW 1
+#define LH_BQ64_WAVES 4
+#define LH_BQ128_WAVES 8
+#define LH_BQ_MINW 2
+#endif
+
 namespace lh {
 
 namespace {
@@ -49,12 +73,79 @@ __device__ __forceinline__ f32x16 zero16() {
   return z;
 }
 
-// A operand from a transposed LDS tile: row `r` of the tile, runs at column
-// col and col + 8 (4 elements each).
-__device__ __forceinline__ bf16x8 load_tr(const __bf16* tile, int stride, int r, int col) {
-  const __bf16* p = tile + r * stride + col;
-  const bf16x4 lo = *reinterpret_cast<const bf16x4*>(p);
-  const bf16x4 hi = *reinterpret_cast<const bf16x4*>(p + 8);
+// ------------------------------------------------------------------ tiles
+//
+// K/V/Q/dO tiles are staged row-major in LDS by direct global->LDS loads
+// (global_load_lds, 16 bytes per lane: lane l of one instruction lands at
+// byte 16*l of a 1 KB run).  Rows hold d/8 16-byte chunks whose order is
+// XOR-swizzled per row, so that both the row reads of an MFMA A operand
+// (16 rows, same chunk) and the transposed reads below hit distinct banks.
+//
+// Transposed operands come from ds_read_tr16_b64: within each 16-lane group,
+// lane i receives element i%4 of the 8-byte reads of lanes i/4, 4+i/4, 8+i/4
+// and 12+i/4.  Pointing lane j at row r0 + j/4, columns c0 + 4*(j%4) .. +3
+// therefore hands lane i the four rows r0..r0+3 of column c0 + i.
+
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (D == 64) return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+  else return ((r & 3) << 2) | ((r >> 2) & 3);
+}
+
+// byte offset of logical 16-byte chunk x of row r in a swizzled tile
+template <int D>
+__device__ __forceinline__ int toff(int r, int x) {
+  return r * (D * 2) + ((x ^ swz<D>(r)) << 4);
+}
+
+// Asynchronously copy rows [r0, r0 + R) of a [S][D] bf16 tensor into a
+// swizzled LDS tile; rows >= S repeat row S-1 (they are masked or unused).
+// Waves w = wave, wave + NW, ... of the workgroup split the instructions.
+template <int D, int R, int NW>
+__device__ __forceinline__ void load_tile(const __bf16* src, int S, int r0, __bf16* tile, int wave,
+                                          int lane) {
+  constexpr int kCPR = D / 8;
+  constexpr int kInst = R * kCPR / 64;
+#pragma unroll
+  for (int n = wave; n < kInst; n += NW) {
+    const int p = n * 64 + lane;
+    const int r = p / kCPR, pc = p % kCPR;
+    const int x = pc ^ swz<D>(r);
+    const int row = min(r0 + r, S - 1);
+    __builtin_amdgcn_global_load_lds(src + (int64_t)row * D + x * 8,
+                                     (lds_void*)(tile + n * 512), 16, 0, 0);
+  }
+}
+
+__device__ __forceinline__ void wait_loads() { __builtin_amdgcn_s_waitcnt(0); }
+
+// A operand from rows (MFMA row = tile row r, contraction = 8 elements of
+// logical chunk x)
+template <int D>
+__device__ __forceinline__ bf16x8 rd_rows(const __bf16* tile, int r, int x) {
+  return *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(tile) + toff<D>(r, x));
+}
+
+// A operand transposed: lane (h, c) of the wave gets column c0 + c%16 + 16*(c/16)
+// ... precisely: lane l (group G = l/16, j = l%16) reads row r0 + j/4 at
+// columns cb + 16*(G&1) + 4*(j%4); the result holds column cb + (l%32) of
+// rows r0..r0+3.  Two such reads (rows r0 and r0 + 8) form one operand.
+template <int D>
+__device__ __forceinline__ bf16x4 rd_tr(const __bf16* tile, int r0, int cb, int lane) {
+  const int j = lane & 15, G = lane >> 4;
+  const int r = r0 + (j >> 2);
+  const int col = cb + 16 * (G & 1) + 4 * (j & 3);
+  const char* p = reinterpret_cast<const char*>(tile) + toff<D>(r, col >> 3) + ((col & 7) << 1);
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p);
+}
+
+template <int D>
+__device__ __forceinline__ bf16x8 rd_tr8(const __bf16* tile, int r0, int cb, int lane) {
+  const bf16x4 lo = rd_tr<D>(tile, r0, cb, lane);
+  const bf16x4 hi = rd_tr<D>(tile, r0 + 8, cb, lane);
   bf16x8 a;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
@@ -64,132 +155,147 @@ __device__ __forceinline__ bf16x8 load_tr(const __bf16* tile, int stride, int r,
   return a;
 }
 
-// Stage rows [r0, r0+R) of a [S][D] tensor into LDS row-major (stride RS)
-// and/or transposed (tile[dim][row], stride TS); rows >= S read as zero.
-template <int D, int R, int NTHR>
-__device__ __forceinline__ void stage_rows(const __bf16* src, int S, int r0, __bf16* rowmajor,
-                                           int RS, __bf16* transposed, int TS, int tid) {
-  constexpr int kUnits = (R / 4) * (D / 8);  // 4 rows x 8 dims per unit
-  for (int u = tid; u < kUnits; u += NTHR) {
-    const int rg = u / (D / 8), dg = u % (D / 8);
-    bf16x8 r[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = r0 + 4 * rg + i;
-      r[i] = row < S ? *reinterpret_cast<const bf16x8*>(src + (int64_t)row * D + dg * 8) : zero8();
-      if (rowmajor) *reinterpret_cast<bf16x8*>(rowmajor + (4 * rg + i) * RS + dg * 8) = r[i];
-    }
-    if (transposed) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        bf16x4 t;
-        t[0] = r[0][e];
-        t[1] = r[1][e];
-        t[2] = r[2][e];
-        t[3] = r[3][e];
-        *reinterpret_cast<bf16x4*>(transposed + (dg * 8 + e) * TS + 4 * rg) = t;
-      }
-    }
+// ------------------------------------------------------------------ grid
+//
+// One-dimensional grids: workgroup p of T runs on XCD p % 8 (workgroups are
+// handed to the eight XCDs round robin).  When the heads split evenly over
+// the XCDs, workgroups are remapped so that every XCD owns BH/8 heads and
+// walks their query blocks heaviest first (latest queries first, since a
+// causal query block costs in proportion to its position), interleaving its
+// heads.  Workgroups running together on an XCD then stream the same K/V
+// tiles through that XCD's L2 instead of all heads' tiles.
+__device__ __forceinline__ void map_block(int p, int T, int BH, int nqb, int& head, int& qblk) {
+  if ((BH & 7) == 0) {
+    const int x = p & 7, local = p >> 3;
+    const int hpx = BH >> 3;
+    head = x * hpx + local % hpx;
+    qblk = nqb - 1 - local / hpx;
+  } else {
+    head = p % BH;
+    qblk = nqb - 1 - p / BH;
   }
+  (void)T;
 }
 
 // ------------------------------------------------------------------ forward
+//
+// Online softmax with lazy rescaling: a row keeps its running maximum m
+// until a tile raises it by more than 2^8 (in exp2 units); until then
+// probabilities exp2(s - m) may exceed 1 by at most that factor, which
+// float32 sums and bf16 operands hold exactly as well.  The decision is taken
+// for the whole wave, so the rescale of the accumulators is a uniform branch
+// that is skipped on almost every tile.
 
-template <int D>
+constexpr float kLazyRescale = 8.0f;
+
+template <int D, int QW, int WAVES>
 struct FwdCfg {
-  static constexpr int kWaves = 2;
-  static constexpr int kQW = 64;                 // queries per wave (2 x 32)
-  static constexpr int kQB = kWaves * kQW;       // queries per workgroup
+  static constexpr int kQW = QW;                 // queries per wave
+  static constexpr int kNQB = QW / 32;           // 32-query blocks per wave
+  static constexpr int kWaves = WAVES;
+  static constexpr int kQB = WAVES * QW;         // queries per workgroup
   static constexpr int kKT = 64;                 // keys per tile
-  static constexpr int kKS = D + 8;              // K tile row stride (elements)
-  static constexpr int kVS = kKT + 4;            // V^T tile row stride
+  static constexpr int kTile = kKT * D;          // elements per K or V tile
+  static constexpr int kThreads = 64 * WAVES;
 };
 
-template <int D>
-__global__ __launch_bounds__(128) void attn_fwd_bf16(const __bf16* __restrict__ Q,
-                                                     const __bf16* __restrict__ K,
-                                                     const __bf16* __restrict__ V,
-                                                     float* __restrict__ O,
-                                                     float* __restrict__ LSE, int S, float sl2) {
-  using C = FwdCfg<D>;
-  __shared__ __attribute__((aligned(16))) __bf16 sK[C::kKT * C::kKS];
-  __shared__ __attribute__((aligned(16))) __bf16 sVt[D * C::kVS];
+template <int D, int QW, int WAVES, int MINW>
+__global__ __launch_bounds__(64 * WAVES, MINW) void attn_fwd_bf16(
+    const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
+    float* __restrict__ O, float* __restrict__ LSE, int S, float sl2) {
+  using C = FwdCfg<D, QW, WAVES>;
+  constexpr int NQB = C::kNQB;
+  __shared__ __attribute__((aligned(1024))) __bf16 sKV[2][2][C::kTile];  // [buffer][K,V]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, c32 = lane & 31;
-  const int64_t bh = blockIdx.y;
-  const int qblk = gridDim.x - 1 - blockIdx.x;  // late (heavy) query blocks first
+  const int nqb = (S + C::kQB - 1) / C::kQB;
+  int head, qblk;
+  map_block(blockIdx.x, gridDim.x, gridDim.x / nqb, nqb, head, qblk);
+  const int64_t bh = head;
   const int q0 = qblk * C::kQB;
   const int qw0 = q0 + wave * C::kQW;
   const __bf16* Qh = Q + bh * (int64_t)S * D;
   const __bf16* Kh = K + bh * (int64_t)S * D;
   const __bf16* Vh = V + bh * (int64_t)S * D;
 
-  bf16x8 qreg[2][D / 16];
+  const int kend = min(S, q0 + C::kQB);
+  const int ntiles = (kend + C::kKT - 1) / C::kKT;
+  load_tile<D, C::kKT, WAVES>(Kh, S, 0, sKV[0][0], wave, lane);
+  load_tile<D, C::kKT, WAVES>(Vh, S, 0, sKV[0][1], wave, lane);
+
+  bf16x8 qreg[NQB][D / 16];
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
+  for (int qb = 0; qb < NQB; ++qb) {
     const int row = qw0 + qb * 32 + c32;
 #pragma unroll
     for (int dc = 0; dc < D / 16; ++dc)
       qreg[qb][dc] = row < S ? *reinterpret_cast<const bf16x8*>(Qh + (int64_t)row * D + dc * 16 + 8 * h)
                              : zero8();
   }
-  f32x16 oacc[2][D / 32];
+  f32x16 oacc[NQB][D / 32];
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb)
+  for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
     for (int mb = 0; mb < D / 32; ++mb) oacc[qb][mb] = zero16();
-  float mrow[2] = {neg_inf(), neg_inf()};
-  float lsum[2] = {0.f, 0.f};
+  float mrow[NQB], lsum[NQB];   // running max (exp2 units) and sum per query
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb) {
+    mrow[qb] = neg_inf();
+    lsum[qb] = 0.f;
+  }
 
-  const int kend = min(S, q0 + C::kQB);
-  const int ntiles = (kend + C::kKT - 1) / C::kKT;
   for (int kt = 0; kt < ntiles; ++kt) {
     const int k0 = kt * C::kKT;
-    __syncthreads();
-    stage_rows<D, C::kKT, 128>(Kh, S, k0, sK, C::kKS, nullptr, 0, tid);
-    stage_rows<D, C::kKT, 128>(Vh, S, k0, nullptr, 0, sVt, C::kVS, tid);
-    __syncthreads();
-    if (qw0 >= S || k0 > qw0 + C::kQW - 1) continue;  // nothing visible for this wave
-
-    f32x16 sacc[2][2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) sacc[kb][qb] = zero16();
-#pragma unroll
-    for (int dc = 0; dc < D / 16; ++dc) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(sK + (kb * 32 + c32) * C::kKS + dc * 16 + 8 * h);
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) sacc[kb][qb] = mfma32(a, qreg[qb][dc], sacc[kb][qb]);
-      }
+    wait_loads();
+    __syncthreads();  // tile kt is in LDS; buffer (kt+1)&1 is free
+    if (kt + 1 < ntiles) {
+      load_tile<D, C::kKT, WAVES>(Kh, S, k0 + C::kKT, sKV[(kt + 1) & 1][0], wave, lane);
+      load_tile<D, C::kKT, WAVES>(Vh, S, k0 + C::kKT, sKV[(kt + 1) & 1][1], wave, lane);
     }
+    if (qw0 >= S || k0 > qw0 + C::kQW - 1) continue;  // nothing visible for this wave
+    const __bf16* sK = sKV[kt & 1][0];
+    const __bf16* sV = sKV[kt & 1][1];
 
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int qb = 0; qb < NQB; ++qb) {
       const int qbase = qw0 + qb * 32;
       if (k0 > qbase + 31) continue;
+      f32x16 sacc[2] = {zero16(), zero16()};
+#pragma unroll
+      for (int dc = 0; dc < D / 16; ++dc)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+          sacc[kb] = mfma32(rd_rows<D>(sK, kb * 32 + c32, 2 * dc + h), qreg[qb][dc], sacc[kb]);
       const int query = qbase + c32;
-      const bool diag = k0 + C::kKT - 1 > qbase;
       float mx = neg_inf();
+      if (k0 + C::kKT - 1 > qbase) {  // diagonal tile: causal mask
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = k0 + kb * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
-          float s = sacc[kb][qb][i] * sl2;
-          if (diag && key > query) s = neg_inf();
-          sacc[kb][qb][i] = s;
-          mx = fmaxf(mx, s);
-        }
+          for (int i = 0; i < 16; ++i) {
+            const int key = k0 + kb * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
+            sacc[kb][i] = key > query ? neg_inf() : sacc[kb][i] * sl2;
+            mx = fmaxf(mx, sacc[kb][i]);
+          }
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            sacc[kb][i] *= sl2;
+            mx = fmaxf(mx, sacc[kb][i]);
+          }
+      }
       mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mnew = fmaxf(mrow[qb], mx);
-      const float alpha = fexp2(mrow[qb] - mnew);
-      mrow[qb] = mnew;
-      lsum[qb] *= alpha;
+      if (__any(mx > mrow[qb] + kLazyRescale)) {  // wave-uniform
+        const float mnew = fmaxf(mrow[qb], mx);
+        const float alpha = fexp2(mrow[qb] - mnew);
+        lsum[qb] *= alpha;
 #pragma unroll
-      for (int mb = 0; mb < D / 32; ++mb) oacc[qb][mb] *= alpha;
+        for (int mb = 0; mb < D / 32; ++mb) oacc[qb][mb] *= alpha;
+        mrow[qb] = mnew;
+      }
+      const float m = mrow[qb];
       bf16x8 pk[2][2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -197,7 +303,7 @@ __global__ __launch_bounds__(128) void attn_fwd_bf16(const __bf16* __restrict__ 
         for (int c = 0; c < 2; ++c)
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            const float pv = fexp2(sacc[kb][qb][8 * c + e] - mnew);
+            const float pv = fexp2(sacc[kb][8 * c + e] - m);
             lsum[qb] += pv;
             pk[kb][c][e] = static_cast<__bf16>(pv);
           }
@@ -206,10 +312,9 @@ __global__ __launch_bounds__(128) void attn_fwd_bf16(const __bf16* __restrict__ 
 #pragma unroll
         for (int c = 0; c < 2; ++c)
 #pragma unroll
-          for (int mb = 0; mb < D / 32; ++mb) {
-            const bf16x8 a = load_tr(sVt, C::kVS, mb * 32 + c32, kb * 32 + 16 * c + 4 * h);
-            oacc[qb][mb] = mfma32(a, pk[kb][c], oacc[qb][mb]);
-          }
+          for (int mb = 0; mb < D / 32; ++mb)
+            oacc[qb][mb] = mfma32(rd_tr8<D>(sV, kb * 32 + 16 * c + 4 * h, mb * 32, lane),
+                                  pk[kb][c], oacc[qb][mb]);
     }
   }
 
@@ -217,7 +322,7 @@ __global__ __launch_bounds__(128) void attn_fwd_bf16(const __bf16* __restrict__ 
   float* Oh = O + bh * (int64_t)S * D;
   float* Lh = LSE + bh * (int64_t)S;
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
+  for (int qb = 0; qb < NQB; ++qb) {
     const float lt = lsum[qb] + __shfl_xor(lsum[qb], 32);
     const float inv = 1.0f / lt;
     const int query = qw0 + qb * 32 + c32;
@@ -261,34 +366,57 @@ __global__ __launch_bounds__(256) void attn_delta(const float* __restrict__ O, c
   if (row < rows && lane == 0) delta[row] = s;
 }
 
-template <int D>
+// Stage 64 float32 values (lse or delta of a query tile) into LDS with one
+// direct load (4 bytes per lane); rows >= S repeat row S-1.
+__device__ __forceinline__ void load_vec64(const float* src, int S, int r0, float* dst, int lane) {
+  __builtin_amdgcn_global_load_lds(src + min(r0 + lane, S - 1), (lds_void*)dst, 4, 0, 0);
+}
+
+// Key-block pass: each wave keeps 32 keys (K and V rows as MFMA B operands)
+// and walks the query tiles from its block's diagonal to the end, producing
+// dK and dV with no atomics.  Per 32-query slice:
+//   S = Q K^T, dP = dO V^T         (A = Q / dO rows from LDS)
+//   P = exp2(S*scale*log2e - lse*log2e), dS = P (dP - delta)
+//   dV^T += dO^T P, dK^T += Q^T dS  (A = transposed reads of the Q / dO tiles)
+template <int D, int WAVES>
 struct BwdKVCfg {
-  static constexpr int kWaves = 4;
-  static constexpr int kKW = 32;            // keys per wave
-  static constexpr int kKB = kWaves * kKW;  // keys per workgroup
-  static constexpr int kQT = 64;            // queries per tile
-  static constexpr int kRS = D + 8;
-  static constexpr int kTS = kQT + 4;
+  static constexpr int kKW = 32;
+  static constexpr int kKB = WAVES * kKW;  // keys per workgroup
+  static constexpr int kQT = 64;           // queries per tile
+  static constexpr int kTile = kQT * D;
 };
 
-template <int D>
-__global__ __launch_bounds__(256) void attn_bwd_dkdv_bf16(
+template <int D, int WAVES, int MINW>
+__global__ __launch_bounds__(64 * WAVES, MINW) void attn_bwd_dkdv_bf16(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     const __bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ DELTA,
     float* __restrict__ dK, float* __restrict__ dV, int S, float sl2, float scale) {
-  using C = BwdKVCfg<D>;
-  __shared__ __attribute__((aligned(16))) __bf16 sQ[C::kQT * C::kRS];
-  __shared__ __attribute__((aligned(16))) __bf16 sdO[C::kQT * C::kRS];
-  __shared__ __attribute__((aligned(16))) __bf16 sQt[D * C::kTS];
-  __shared__ __attribute__((aligned(16))) __bf16 sdOt[D * C::kTS];
-  __shared__ float sL[C::kQT], sDl[C::kQT];
+  using C = BwdKVCfg<D, WAVES>;
+  __shared__ __attribute__((aligned(1024))) __bf16 sT[2][2][C::kTile];  // [buffer][Q, dO]
+  __shared__ float sLD[2][2][C::kQT];                                  // [buffer][lse, delta]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, c32 = lane & 31;
-  const int64_t bh = blockIdx.y;
-  const int kb0 = blockIdx.x * C::kKB;
+  const int nkb = (S + C::kKB - 1) / C::kKB;
+  int head, rank;
+  map_block(blockIdx.x, gridDim.x, gridDim.x / nkb, nkb, head, rank);
+  const int kblk = nkb - 1 - rank;  // early keys (most queries) first
+  const int64_t bh = head;
+  const int kb0 = kblk * C::kKB;
   const int kw0 = kb0 + wave * C::kKW;
   const int key = kw0 + c32;
   const int64_t off = bh * (int64_t)S * D;
+  const float* lse_h = LSE + bh * (int64_t)S;
+  const float* del_h = DELTA + bh * (int64_t)S;
+
+  const int t0 = kb0 / C::kQT;
+  const int ntiles = (S + C::kQT - 1) / C::kQT;
+  auto issue = [&](int t, int buf) {
+    load_tile<D, C::kQT, WAVES>(Q + off, S, t * C::kQT, sT[buf][0], wave, lane);
+    load_tile<D, C::kQT, WAVES>(dO + off, S, t * C::kQT, sT[buf][1], wave, lane);
+    if (wave == 0) load_vec64(lse_h, S, t * C::kQT, sLD[buf][0], lane);
+    if (wave == WAVES - 1) load_vec64(del_h, S, t * C::kQT, sLD[buf][1], lane);
+  };
+  issue(t0, 0);
 
   bf16x8 kreg[D / 16], vreg[D / 16];
 #pragma unroll
@@ -303,17 +431,17 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_bf16(
     dva[mb] = zero16();
   }
 
-  for (int q0 = (kb0 / C::kQT) * C::kQT; q0 < S; q0 += C::kQT) {
+  for (int t = t0; t < ntiles; ++t) {
+    const int buf = (t - t0) & 1;
+    const int q0 = t * C::kQT;
+    wait_loads();
     __syncthreads();
-    stage_rows<D, C::kQT, 256>(Q + off, S, q0, sQ, C::kRS, sQt, C::kTS, tid);
-    stage_rows<D, C::kQT, 256>(dO + off, S, q0, sdO, C::kRS, sdOt, C::kTS, tid);
-    if (tid < C::kQT) {
-      const int q = q0 + tid;
-      sL[tid] = q < S ? LSE[bh * (int64_t)S + q] * kLog2e : 0.f;
-      sDl[tid] = q < S ? DELTA[bh * (int64_t)S + q] : 0.f;
-    }
-    __syncthreads();
+    if (t + 1 < ntiles) issue(t + 1, buf ^ 1);
     if (kw0 >= S || q0 + C::kQT - 1 < kw0) continue;
+    const __bf16* sQ = sT[buf][0];
+    const __bf16* sG = sT[buf][1];
+    const float* sL = sLD[buf][0];
+    const float* sD = sLD[buf][1];
 #pragma unroll
     for (int qs = 0; qs < 2; ++qs) {
       const int qbase = q0 + qs * 32;
@@ -321,27 +449,27 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_bf16(
       f32x16 sacc = zero16(), dpacc = zero16();
 #pragma unroll
       for (int dc = 0; dc < D / 16; ++dc) {
-        const int o = (qs * 32 + c32) * C::kRS + dc * 16 + 8 * h;
-        sacc = mfma32(*reinterpret_cast<const bf16x8*>(sQ + o), kreg[dc], sacc);
-        dpacc = mfma32(*reinterpret_cast<const bf16x8*>(sdO + o), vreg[dc], dpacc);
+        sacc = mfma32(rd_rows<D>(sQ, qs * 32 + c32, 2 * dc + h), kreg[dc], sacc);
+        dpacc = mfma32(rd_rows<D>(sG, qs * 32 + c32, 2 * dc + h), vreg[dc], dpacc);
       }
+      const bool diag = qbase < kw0 + 31;
       bf16x8 pch[2], dsch[2];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int qi = qs * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
-        const int query = q0 + qi;
-        const float p = (key <= query && query < S) ? fexp2(sacc[i] * sl2 - sL[qi]) : 0.f;
-        const float ds = p * (dpacc[i] - sDl[qi]);
+        float p = fexp2(__builtin_fmaf(sacc[i], sl2, -sL[qi] * kLog2e));
+        if (diag && key > q0 + qi) p = 0.f;
+        if (q0 + qi >= S) p = 0.f;
         pch[i >> 3][i & 7] = static_cast<__bf16>(p);
-        dsch[i >> 3][i & 7] = static_cast<__bf16>(ds);
+        dsch[i >> 3][i & 7] = static_cast<__bf16>(p * (dpacc[i] - sD[qi]));
       }
 #pragma unroll
       for (int c = 0; c < 2; ++c)
 #pragma unroll
         for (int mb = 0; mb < D / 32; ++mb) {
-          const int col = qs * 32 + 16 * c + 4 * h;
-          dva[mb] = mfma32(load_tr(sdOt, C::kTS, mb * 32 + c32, col), pch[c], dva[mb]);
-          dka[mb] = mfma32(load_tr(sQt, C::kTS, mb * 32 + c32, col), dsch[c], dka[mb]);
+          const int r0 = qs * 32 + 16 * c + 4 * h;
+          dva[mb] = mfma32(rd_tr8<D>(sG, r0, mb * 32, lane), pch[c], dva[mb]);
+          dka[mb] = mfma32(rd_tr8<D>(sQ, r0, mb * 32, lane), dsch[c], dka[mb]);
         }
     }
   }
@@ -362,33 +490,40 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_bf16(
     }
 }
 
-template <int D>
+// Query-block pass: each wave keeps 32 queries (Q and dO rows as B operands,
+// lse and delta in registers) and walks the key tiles up to its diagonal:
+//   S^T = K Q^T, dP^T = V dO^T      (A = K / V rows from LDS)
+//   dS^T = P^T (dP^T - delta), dQ^T += K^T dS^T (A = transposed reads of K)
+template <int D, int WAVES>
 struct BwdQCfg {
-  static constexpr int kWaves = 4;
   static constexpr int kQW = 32;
-  static constexpr int kQB = kWaves * kQW;
+  static constexpr int kQB = WAVES * kQW;
   static constexpr int kKT = 64;
-  static constexpr int kRS = D + 8;
-  static constexpr int kTS = kKT + 4;
+  static constexpr int kTile = kKT * D;
 };
 
-template <int D>
-__global__ __launch_bounds__(256) void attn_bwd_dq_bf16(
+template <int D, int WAVES, int MINW>
+__global__ __launch_bounds__(64 * WAVES, MINW) void attn_bwd_dq_bf16(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     const __bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ DELTA,
     float* __restrict__ dQ, int S, float sl2, float scale) {
-  using C = BwdQCfg<D>;
-  __shared__ __attribute__((aligned(16))) __bf16 sK[C::kKT * C::kRS];
-  __shared__ __attribute__((aligned(16))) __bf16 sV[C::kKT * C::kRS];
-  __shared__ __attribute__((aligned(16))) __bf16 sKt[D * C::kTS];
+  using C = BwdQCfg<D, WAVES>;
+  __shared__ __attribute__((aligned(1024))) __bf16 sKV[2][2][C::kTile];  // [buffer][K, V]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, c32 = lane & 31;
-  const int64_t bh = blockIdx.y;
-  const int qblk = gridDim.x - 1 - blockIdx.x;
+  const int nqb = (S + C::kQB - 1) / C::kQB;
+  int head, qblk;
+  map_block(blockIdx.x, gridDim.x, gridDim.x / nqb, nqb, head, qblk);
+  const int64_t bh = head;
   const int q0 = qblk * C::kQB;
   const int qw0 = q0 + wave * C::kQW;
   const int query = qw0 + c32;
   const int64_t off = bh * (int64_t)S * D;
+
+  const int kend = min(S, q0 + C::kQB);
+  const int ntiles = (kend + C::kKT - 1) / C::kKT;
+  load_tile<D, C::kKT, WAVES>(K + off, S, 0, sKV[0][0], wave, lane);
+  load_tile<D, C::kKT, WAVES>(V + off, S, 0, sKV[0][1], wave, lane);
 
   bf16x8 qreg[D / 16], doreg[D / 16];
 #pragma unroll
@@ -402,13 +537,17 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_bf16(
 #pragma unroll
   for (int mb = 0; mb < D / 32; ++mb) dqa[mb] = zero16();
 
-  const int kend = min(S, q0 + C::kQB);
-  for (int k0 = 0; k0 < kend; k0 += C::kKT) {
+  for (int kt = 0; kt < ntiles; ++kt) {
+    const int k0 = kt * C::kKT;
+    wait_loads();
     __syncthreads();
-    stage_rows<D, C::kKT, 256>(K + off, S, k0, sK, C::kRS, sKt, C::kTS, tid);
-    stage_rows<D, C::kKT, 256>(V + off, S, k0, sV, C::kRS, nullptr, 0, tid);
-    __syncthreads();
+    if (kt + 1 < ntiles) {
+      load_tile<D, C::kKT, WAVES>(K + off, S, k0 + C::kKT, sKV[(kt + 1) & 1][0], wave, lane);
+      load_tile<D, C::kKT, WAVES>(V + off, S, k0 + C::kKT, sKV[(kt + 1) & 1][1], wave, lane);
+    }
     if (qw0 >= S || k0 > qw0 + C::kQW - 1) continue;
+    const __bf16* sK = sKV[kt & 1][0];
+    const __bf16* sV = sKV[kt & 1][1];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const int kbase = k0 + kb * 32;
@@ -416,23 +555,23 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_bf16(
       f32x16 sacc = zero16(), dpacc = zero16();
 #pragma unroll
       for (int dc = 0; dc < D / 16; ++dc) {
-        const int o = (kb * 32 + c32) * C::kRS + dc * 16 + 8 * h;
-        sacc = mfma32(*reinterpret_cast<const bf16x8*>(sK + o), qreg[dc], sacc);
-        dpacc = mfma32(*reinterpret_cast<const bf16x8*>(sV + o), doreg[dc], dpacc);
+        sacc = mfma32(rd_rows<D>(sK, kb * 32 + c32, 2 * dc + h), qreg[dc], sacc);
+        dpacc = mfma32(rd_rows<D>(sV, kb * 32 + c32, 2 * dc + h), doreg[dc], dpacc);
       }
+      const bool diag = kbase + 31 > qw0;
       bf16x8 dsch[2];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int key = kbase + 8 * (i >> 2) + 4 * h + (i & 3);
-        const float p = key <= query ? fexp2(sacc[i] * sl2 - lse2) : 0.f;
+        const int kk = kbase + 8 * (i >> 2) + 4 * h + (i & 3);
+        float p = fexp2(__builtin_fmaf(sacc[i], sl2, -lse2));
+        if (diag && kk > query) p = 0.f;
         dsch[i >> 3][i & 7] = static_cast<__bf16>(p * (dpacc[i] - dl));
       }
 #pragma unroll
       for (int c = 0; c < 2; ++c)
 #pragma unroll
         for (int mb = 0; mb < D / 32; ++mb)
-          dqa[mb] = mfma32(load_tr(sKt, C::kTS, mb * 32 + c32, kb * 32 + 16 * c + 4 * h), dsch[c],
-                           dqa[mb]);
+          dqa[mb] = mfma32(rd_tr8<D>(sK, kb * 32 + 16 * c + 4 * h, mb * 32, lane), dsch[c], dqa[mb]);
     }
   }
   if (query >= S) return;
@@ -468,11 +607,15 @@ hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, float* o
   const auto K = static_cast<const __bf16*>(k);
   const auto V = static_cast<const __bf16*>(v);
   if (d == 64) {
-    const dim3 grid((unsigned)((S + FwdCfg<64>::kQB - 1) / FwdCfg<64>::kQB), (unsigned)BH);
-    attn_fwd_bf16<64><<<grid, 128, 0, st>>>(Q, K, V, o, lse, (int)S, sl2);
+    using C = FwdCfg<64, LH_FWD64_QW, LH_FWD64_WAVES>;
+    const dim3 grid((unsigned)((S + C::kQB - 1) / C::kQB * BH));
+    attn_fwd_bf16<64, LH_FWD64_QW, LH_FWD64_WAVES, LH_FWD64_MINW><<<grid, C::kThreads, 0, st>>>(
+        Q, K, V, o, lse, (int)S, sl2);
   } else {
-    const dim3 grid((unsigned)((S + FwdCfg<128>::kQB - 1) / FwdCfg<128>::kQB), (unsigned)BH);
-    attn_fwd_bf16<128><<<grid, 128, 0, st>>>(Q, K, V, o, lse, (int)S, sl2);
+    using C = FwdCfg<128, LH_FWD128_QW, LH_FWD128_WAVES>;
+    const dim3 grid((unsigned)((S + C::kQB - 1) / C::kQB * BH));
+    attn_fwd_bf16<128, LH_FWD128_QW, LH_FWD128_WAVES, LH_FWD128_MINW><<<grid, C::kThreads, 0, st>>>(
+        Q, K, V, o, lse, (int)S, sl2);
   }
   return hipGetLastError();
 }
@@ -504,21 +647,29 @@ hipError_t launch_attn_bwd(const void* q, const void* k, const void* v, const fl
   const auto V = static_cast<const __bf16*>(v);
   const auto G = static_cast<const __bf16*>(dout);
   if (d == 64) {
-    const dim3 g1((unsigned)((S + BwdKVCfg<64>::kKB - 1) / BwdKVCfg<64>::kKB), (unsigned)BH);
-    attn_bwd_dkdv_bf16<64><<<g1, 256, 0, st>>>(Q, K, V, G, lse, delta, dk, dv, (int)S, sl2, scale);
+    using C1 = BwdKVCfg<64, LH_BKV64_WAVES>;
+    const dim3 g1((unsigned)((S + C1::kKB - 1) / C1::kKB * BH));
+    attn_bwd_dkdv_bf16<64, LH_BKV64_WAVES, LH_BKV64_MINW><<<g1, 64 * LH_BKV64_WAVES, 0, st>>>(
+        Q, K, V, G, lse, delta, dk, dv, (int)S, sl2, scale);
   } else {
-    const dim3 g1((unsigned)((S + BwdKVCfg<128>::kKB - 1) / BwdKVCfg<128>::kKB), (unsigned)BH);
-    attn_bwd_dkdv_bf16<128><<<g1, 256, 0, st>>>(Q, K, V, G, lse, delta, dk, dv, (int)S, sl2, scale);
+    using C1 = BwdKVCfg<128, LH_BKV128_WAVES>;
+    const dim3 g1((unsigned)((S + C1::kKB - 1) / C1::kKB * BH));
+    attn_bwd_dkdv_bf16<128, LH_BKV128_WAVES, LH_BKV128_MINW><<<g1, 64 * LH_BKV128_WAVES, 0, st>>>(
+        Q, K, V, G, lse, delta, dk, dv, (int)S, sl2, scale);
   }
   e = hipGetLastError();
   if (e == hipSuccess && ev) e = hipEventRecord(ev[1], st);
   if (e != hipSuccess) return e;
   if (d == 64) {
-    const dim3 g2((unsigned)((S + BwdQCfg<64>::kQB - 1) / BwdQCfg<64>::kQB), (unsigned)BH);
-    attn_bwd_dq_bf16<64><<<g2, 256, 0, st>>>(Q, K, V, G, lse, delta, dq, (int)S, sl2, scale);
+    using C2 = BwdQCfg<64, LH_BQ64_WAVES>;
+    const dim3 g2((unsigned)((S + C2::kQB - 1) / C2::kQB * BH));
+    attn_bwd_dq_bf16<64, LH_BQ64_WAVES, LH_BQ_MINW><<<g2, 64 * LH_BQ64_WAVES, 0, st>>>(
+        Q, K, V, G, lse, delta, dq, (int)S, sl2, scale);
   } else {
-    const dim3 g2((unsigned)((S + BwdQCfg<128>::kQB - 1) / BwdQCfg<128>::kQB), (unsigned)BH);
-    attn_bwd_dq_bf16<128><<<g2, 256, 0, st>>>(Q, K, V, G, lse, delta, dq, (int)S, sl2, scale);
+    using C2 = BwdQCfg<128, LH_BQ128_WAVES>;
+    const dim3 g2((unsigned)((S + C2::kQB - 1) / C2::kQB * BH));
+    attn_bwd_dq_bf16<128, LH_BQ128_WAVES, LH_BQ_MINW><<<g2, 64 * LH_BQ128_WAVES, 0, st>>>(
+        Q, K, V, G, lse, delta, dq, (int)S, sl2, scale);
   }
   e = hipGetLastError();
   if (e == hipSuccess && ev) e = hipEventRecord(ev[2], st);
