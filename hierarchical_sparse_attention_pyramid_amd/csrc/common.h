@@ -21,6 +21,7 @@ struct Geo {
   int32_t base[kMaxLevels];      // flat index of the first entry of level l
   int32_t pw[kMaxLevels];        // p^l
   int32_t nlev[kMaxLevels];      // N / p^l
+  float inv_pw[kMaxLevels];      // 1 / p^l rounded to float (exact when p is a power of two)
 };
 
 __device__ __forceinline__ int32_t div_pw(int32_t t, const Geo& g, int l) {

@@ -10,7 +10,7 @@
 namespace lh {
 
 // Maximum pyramid levels one pooling pass produces in registers.
-constexpr int kStageLevels = 4;
+constexpr int kStageLevels = 3;
 
 struct PoolFwdArgs {
   const void* in[3];     // stage input: tokens [BH][N][d] (dtype) or f32 sums [BH][in_rows][d]

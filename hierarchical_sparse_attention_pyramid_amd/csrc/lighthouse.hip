@@ -70,12 +70,14 @@ lh_status make_plan(const lh_shape* s, Plan& P) {
     }
     if (s->N % pw) return fail(LH_EINVAL, "N must be divisible by p^(L-1)");
     g.pw[l] = (int32_t)pw;
+    g.inv_pw[l] = (float)(1.0 / (double)pw);
     g.nlev[l] = (int32_t)(s->N / pw);
     g.base[l] = (int32_t)M;
     M += s->N / pw;
   }
   for (int l = s->L; l < lh::kMaxLevels; ++l) {
     g.pw[l] = 0;
+    g.inv_pw[l] = 0.f;
     g.nlev[l] = 0;
     g.base[l] = (int32_t)M;
   }
@@ -115,7 +117,9 @@ lh_status make_plan(const lh_shape* s, Plan& P) {
       const int lam = std::min(s->L - 1 - lvl, lm);
       int64_t plam = 1;
       for (int i = 0; i < lam; ++i) plam *= s->p;
-      const int64_t rep = std::max<int64_t>(1, 64 / plam);
+      // token passes walk 64-row chunks; upper passes see p^lvl times fewer
+      // rows, so they take one span per row group to keep the GPU busy
+      const int64_t rep = lvl == 0 ? std::max<int64_t>(1, 64 / plam) : 1;
       const int64_t rows_in = s->N / g.pw[lvl];
       Stage t{lvl, lam, (int)(plam * rep), rows_in, rows_in / plam, -1};
       P.st[P.nstages++] = t;

@@ -15,10 +15,13 @@
 // pass.  Deep pyramids use several passes: a pass hands the float32 sums of
 // its top level to the next one.
 #include "kernels.h"
+#include "walk.h"
 
 namespace lh {
 
 namespace {
+
+constexpr int kRowsInFlight = 4;  // rows whose loads a row group issues together
 
 // ||x||_2 of a d-long row spread over `lpr` lanes (element 8*lane + e in
 // x[e]), in the fixed float32 order: squares, then the halving tree
@@ -39,17 +42,6 @@ __device__ __forceinline__ float row_norm(const float (&x)[8], int lpr) {
   return sqrtf(c0 + c1);  // correctly rounded on gfx950 (not __fsqrt_rn)
 }
 
-__device__ __forceinline__ void scale8(float (&x)[8], float div, bool pow2) {
-  if (pow2) {
-    const float r = 1.0f / div;  // exact for powers of two
-#pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] *= r;
-  } else {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] = x[e] / div;
-  }
-}
-
 // One pass over the tensors listed in `tid` for the chunk of rows
 // [r0, r0 + nrows) of head bh.  SCORE: 0 none, 1 norms (level 0 input),
 // 2 max-pool of stored level-lvl0 scores.
@@ -60,7 +52,6 @@ __device__ __forceinline__ void pool_pass(const PoolFwdArgs& a, const int (&tid)
   const Geo& g = a.g;
   const int d = g.d;
   const int lpr = d / 8;
-  const bool pow2 = g.log2p >= 0;
   const Tin* in[NT];
   Tout* pyr[NT];
   float* so[NT];
@@ -87,66 +78,79 @@ __device__ __forceinline__ void pool_pass(const PoolFwdArgs& a, const int (&tid)
       for (int e = 0; e < 8; ++e) acc[l][i][e] = 0.f;
   }
 
-  for (int r = 0; r < nrows; ++r) {
-    const int64_t row = r0 + r;
-    float x[NT][8];
+  for (int rb = 0; rb < nrows; rb += kRowsInFlight) {
+    // issue the loads of up to kRowsInFlight rows before using any of them
+    float xs[kRowsInFlight][NT][8];
     if (SCORE == 1 || do_pool) {
 #pragma unroll
-      for (int i = 0; i < NT; ++i) Row8<Tin>::load(in[i] + row * d, x[i]);
-    }
-    float s = 0.f;
-    if constexpr (SCORE == 1) {
-      s = row_norm(x[0], lpr) + row_norm(x[1], lpr);
-      if (lane == 0) score[row] = s;
-    } else if constexpr (SCORE == 2) {
-      s = score[g.base[a.lvl0] + row];
-    }
-    if (do_pool) {
+      for (int u = 0; u < kRowsInFlight; ++u) {
+        const int64_t row = r0 + min(rb + u, nrows - 1);
 #pragma unroll
-      for (int i = 0; i < NT; ++i)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[0][i][e] += x[i][e];
+        for (int i = 0; i < NT; ++i) Row8<Tin>::load(in[i] + row * d, xs[u][i]);
+      }
     }
-    if constexpr (SCORE != 0) smax[0] = fmaxf(smax[0], s);
-
+    float sin[kRowsInFlight];
+    if constexpr (SCORE == 2) {
 #pragma unroll
-    for (int l = 0; l < kStageLevels; ++l) {
-      if (l >= a.lam) break;
-      if (++cnt[l] < g.p) break;
-      cnt[l] = 0;
-      const int lev = a.lvl0 + l + 1;                       // level just completed
-      const int64_t j = (row + 1) / g.pw[l + 1] - 1;        // its index in that level
+      for (int u = 0; u < kRowsInFlight; ++u) sin[u] = score[g.base[a.lvl0] + r0 + min(rb + u, nrows - 1)];
+    }
+#pragma unroll
+    for (int u = 0; u < kRowsInFlight; ++u) {
+      if (rb + u >= nrows) break;
+      const int64_t row = r0 + rb + u;
+      float s = 0.f;
+      if constexpr (SCORE == 1) {
+        s = row_norm(xs[u][0], lpr) + row_norm(xs[u][1], lpr);
+        if (lane == 0) score[row] = s;
+      } else if constexpr (SCORE == 2) {
+        s = sin[u];
+      }
       if (do_pool) {
 #pragma unroll
-        for (int i = 0; i < NT; ++i) {
-          float m[8];
+        for (int i = 0; i < NT; ++i)
 #pragma unroll
-          for (int e = 0; e < 8; ++e) m[e] = acc[l][i][e];
-          scale8(m, static_cast<float>(g.pw[lev]), pow2);
-          Row8<Tout>::store(pyr[i] + (int64_t)(g.base[lev] - g.N + j) * d, m);
-        }
+          for (int e = 0; e < 8; ++e) acc[0][i][e] += xs[u][i][e];
       }
-      if constexpr (SCORE != 0) {
-        if (lane == 0) score[g.base[lev] + j] = smax[l];
-      }
-      if (l + 1 < kStageLevels && l + 1 < a.lam) {
+      if constexpr (SCORE != 0) smax[0] = fmaxf(smax[0], s);
+
+#pragma unroll
+      for (int l = 0; l < kStageLevels; ++l) {
+        if (l >= a.lam) break;
+        if (++cnt[l] < g.p) break;
+        cnt[l] = 0;
+        const int lev = a.lvl0 + l + 1;                       // level just completed
+        const int64_t j = (row + 1) / g.pw[l + 1] - 1;        // its index in that level
         if (do_pool) {
 #pragma unroll
-          for (int i = 0; i < NT; ++i)
+          for (int i = 0; i < NT; ++i) {
+            float m[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) acc[(l + 1) % kStageLevels][i][e] += acc[l][i][e];
+            for (int e = 0; e < 8; ++e) m[e] = acc[l][i][e] * g.inv_pw[lev];
+            Row8<Tout>::store(pyr[i] + (int64_t)(g.base[lev] - g.N + j) * d, m);
+          }
         }
-        if constexpr (SCORE != 0)
-          smax[(l + 1) % kStageLevels] = fmaxf(smax[(l + 1) % kStageLevels], smax[l]);
-      } else if (do_pool && so[0] != nullptr) {
+        if constexpr (SCORE != 0) {
+          if (lane == 0) score[g.base[lev] + j] = smax[l];
+        }
+        if (l + 1 < kStageLevels && l + 1 < a.lam) {
+          if (do_pool) {
 #pragma unroll
-        for (int i = 0; i < NT; ++i) Row8<float>::store(so[i] + j * d, acc[l][i]);
+            for (int i = 0; i < NT; ++i)
+#pragma unroll
+              for (int e = 0; e < 8; ++e) acc[(l + 1) % kStageLevels][i][e] += acc[l][i][e];
+          }
+          if constexpr (SCORE != 0)
+            smax[(l + 1) % kStageLevels] = fmaxf(smax[(l + 1) % kStageLevels], smax[l]);
+        } else if (do_pool && so[0] != nullptr) {
+#pragma unroll
+          for (int i = 0; i < NT; ++i) Row8<float>::store(so[i] + j * d, acc[l][i]);
+        }
+#pragma unroll
+        for (int i = 0; i < NT; ++i)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[l][i][e] = 0.f;
+        smax[l] = neg_inf();
       }
-#pragma unroll
-      for (int i = 0; i < NT; ++i)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[l][i][e] = 0.f;
-      smax[l] = neg_inf();
     }
   }
 }
@@ -178,7 +182,8 @@ __global__ __launch_bounds__(256) void pool_fwd_kernel(PoolFwdArgs a, int do_poo
 
 // Scatter backward: dos[pos(e)] = sum over tokens t of e's span of
 // dout[t] / c_t.  Same row-group walk as the forward; only selected entries
-// are written.
+// are written.  On the token pass, c_t (the number of selected ancestors of
+// t) comes from an ancestor walk that keeps per-level counts.
 template <typename Tin, typename Tout, bool FIRST>
 __global__ __launch_bounds__(256) void pool_bwd_kernel(PoolBwdArgs a) {
   const Geo& g = a.g;
@@ -205,39 +210,48 @@ __global__ __launch_bounds__(256) void pool_bwd_kernel(PoolBwdArgs a) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[l][e] = 0.f;
   }
-  for (int r = 0; r < nrows; ++r) {
-    const int64_t row = r0 + r;
-    float x[8];
-    Row8<Tin>::load(in + row * d, x);
-    if constexpr (FIRST) {
-      const int t = (int)row;
-      int ct = 0;
-      for (int l = 0; l < g.L; ++l) ct += pos[g.base[l] + div_pw(t, g, l)] >= 0;
-      const float rc = 1.0f / static_cast<float>(ct);
+  AncestorWalk<0, 1> walk;
+  for (int rb = 0; rb < nrows; rb += kRowsInFlight) {
+    float xs[kRowsInFlight][8];
+    int32_t pt[kRowsInFlight];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] *= rc;
-      const int32_t pt = pos[t];
-      if (pt >= 0) Row8<Tout>::store(dos + (int64_t)pt * d, x);
+    for (int u = 0; u < kRowsInFlight; ++u) {
+      const int64_t row = r0 + min(rb + u, nrows - 1);
+      Row8<Tin>::load(in + row * d, xs[u]);
+      if constexpr (FIRST) pt[u] = pos[row];
     }
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[0][e] += x[e];
+    for (int u = 0; u < kRowsInFlight; ++u) {
+      if (rb + u >= nrows) break;
+      const int64_t row = r0 + rb + u;
+      if constexpr (FIRST) {
+        walk.advance((int32_t)row, pos, nullptr, g, true, lane);
+        const int ct = walk.cnt[1] + (pt[u] >= 0 ? 1 : 0);
+        const float rc = 1.0f / static_cast<float>(ct);
 #pragma unroll
-    for (int l = 0; l < kStageLevels; ++l) {
-      if (l >= a.lam) break;
-      if (++cnt[l] < g.p) break;
-      cnt[l] = 0;
-      const int lev = a.lvl0 + l + 1;
-      const int64_t j = (row + 1) / g.pw[l + 1] - 1;
-      const int32_t pe = pos[g.base[lev] + j];
-      if (pe >= 0) Row8<Tout>::store(dos + (int64_t)pe * d, acc[l]);
-      if (l + 1 < kStageLevels && l + 1 < a.lam) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[(l + 1) % kStageLevels][e] += acc[l][e];
-      } else if (so != nullptr) {
-        Row8<float>::store(so + j * d, acc[l]);
+        for (int e = 0; e < 8; ++e) xs[u][e] *= rc;
+        if (pt[u] >= 0) Row8<Tout>::store(dos + (int64_t)pt[u] * d, xs[u]);
       }
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[l][e] = 0.f;
+      for (int e = 0; e < 8; ++e) acc[0][e] += xs[u][e];
+#pragma unroll
+      for (int l = 0; l < kStageLevels; ++l) {
+        if (l >= a.lam) break;
+        if (++cnt[l] < g.p) break;
+        cnt[l] = 0;
+        const int lev = a.lvl0 + l + 1;
+        const int64_t j = (row + 1) / g.pw[l + 1] - 1;
+        const int32_t pe = pos[g.base[lev] + j];
+        if (pe >= 0) Row8<Tout>::store(dos + (int64_t)pe * d, acc[l]);
+        if (l + 1 < kStageLevels && l + 1 < a.lam) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[(l + 1) % kStageLevels][e] += acc[l][e];
+        } else if (so != nullptr) {
+          Row8<float>::store(so + j * d, acc[l]);
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[l][e] = 0.f;
+      }
     }
   }
 }

@@ -9,91 +9,105 @@
 //
 // Sources are float32 rows (the attention output, or the float32 gradients
 // of the subsequence); outputs are in the storage type.
-// Both are pulls: every output row is written by exactly one row group, which
-// reads at most L subsequence rows, so the result is deterministic and no
-// atomics are needed.  Coarse rows are shared by up to p^level tokens and are
-// served from cache.
+// Both are pulls: every output row is written by exactly one row group, so
+// the result is deterministic and no atomics are needed.  A row group walks
+// 64 consecutive tokens with an ancestor walk (walk.h): the contribution of
+// an ancestor at level l is loaded once per p^l tokens, and the level-0 loads
+// of four tokens are issued together.  Sums run from the coarsest level down
+// to level 0.
 #include "kernels.h"
+
+#include "walk.h"
 
 namespace lh {
 
 namespace {
 
-constexpr int kTokensPerGroup = 4;
+constexpr int kE = 4;              // elements per lane (16-byte float32 source loads)
+constexpr int kTokPerGroup = 64;   // consecutive tokens walked by one row group
+constexpr int kU = 4;              // tokens whose level-0 loads are issued together
 
-template <typename Tsrc, typename Tout, int NT>
+template <typename Tout> struct Out4;
+template <> struct Out4<float> {
+  static __device__ __forceinline__ void store(float* p, const float (&x)[kE]) {
+    f32x4 v;
+#pragma unroll
+    for (int e = 0; e < kE; ++e) v[e] = x[e];
+    *reinterpret_cast<f32x4*>(p) = v;
+  }
+};
+template <> struct Out4<__bf16> {
+  static __device__ __forceinline__ void store(__bf16* p, const float (&x)[kE]) {
+    bf16x4 v;
+#pragma unroll
+    for (int e = 0; e < kE; ++e) v[e] = static_cast<__bf16>(x[e]);
+    *reinterpret_cast<bf16x4*>(p) = v;
+  }
+};
+
+template <typename Tout, int NT>
 __global__ __launch_bounds__(256) void bcast_kernel(BcastArgs a) {
   const Geo& g = a.g;
-  const int d = g.d;
-  const int lpr = d / 8;
+  const int lpr = g.d / kE;
   const int rgs = 256 / lpr;
   const int rg = threadIdx.x / lpr, lane = threadIdx.x % lpr;
   const int64_t bh = blockIdx.y;
   const int32_t* pos = a.pos + bh * g.M;
-  const Tsrc* src[NT];
+  const bool mean = a.mean != 0;
+  const float* src[NT];
   Tout* out[NT];
 #pragma unroll
   for (int i = 0; i < NT; ++i) {
-    src[i] = a.src[i] + bh * (int64_t)g.S * d + 8 * lane;
-    out[i] = static_cast<Tout*>(a.out[i]) + bh * (int64_t)g.N * d + 8 * lane;
+    src[i] = a.src[i] + bh * (int64_t)g.S * g.d;
+    out[i] = static_cast<Tout*>(a.out[i]) + bh * (int64_t)g.N * g.d + kE * lane;
   }
-  const bool pow2 = g.log2p >= 0;
-  const int64_t t0 = ((int64_t)blockIdx.x * rgs + rg) * kTokensPerGroup;
-  for (int tt = 0; tt < kTokensPerGroup; ++tt) {
-    const int64_t t = t0 + tt;
-    if (t >= g.N) break;
-    float acc[NT][8];
+  const int32_t t0 = ((int32_t)blockIdx.x * rgs + rg) * kTokPerGroup;
+  if (t0 >= g.N) return;  // no block-wide barrier in this kernel
+  const int32_t t1 = min(t0 + kTokPerGroup, g.N);
+  AncestorWalk<NT, kE> w;
+  for (int32_t t = t0; t < t1; t += kU) {
+    int32_t r0[kU];
 #pragma unroll
-    for (int i = 0; i < NT; ++i)
+    for (int u = 0; u < kU; ++u) r0[u] = t + u < t1 ? pos[t + u] : -1;
+    float v0[kU][NT][kE];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[i][e] = 0.f;
-    int cnt = 0;
-    for (int l = 0; l < g.L; ++l) {
-      const int32_t r = pos[g.base[l] + div_pw((int32_t)t, g, l)];
-      if (r < 0) continue;
-      ++cnt;
+    for (int u = 0; u < kU; ++u)
 #pragma unroll
       for (int i = 0; i < NT; ++i) {
-        float v[8];
-        Row8<Tsrc>::load(src[i] + (int64_t)r * d, v);
-        if (a.mean) {
+        f32x4 q = {0.f, 0.f, 0.f, 0.f};
+        if (r0[u] >= 0) q = *reinterpret_cast<const f32x4*>(src[i] + (int64_t)r0[u] * g.d + kE * lane);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) acc[i][e] += v[e];
-        } else if (pow2) {
-          const float w = 1.0f / static_cast<float>(g.pw[l]);  // exact
+        for (int e = 0; e < kE; ++e) v0[u][i][e] = q[e];
+      }
 #pragma unroll
-          for (int e = 0; e < 8; ++e) acc[i][e] += v[e] * w;
-        } else {
-          const float dv = static_cast<float>(g.pw[l]);
+    for (int u = 0; u < kU; ++u) {
+      if (t + u >= t1) break;
+      w.advance(t + u, pos, src, g, mean, lane);
+      const int c = w.cnt[1] + (r0[u] >= 0 ? 1 : 0);
+      const float rc = mean ? 1.0f / static_cast<float>(c) : 1.0f;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) acc[i][e] += v[e] / dv;
-        }
+      for (int i = 0; i < NT; ++i) {
+        float o[kE];
+#pragma unroll
+        for (int e = 0; e < kE; ++e) o[e] = (w.A[1][i][e] + v0[u][i][e]) * rc;
+        Out4<Tout>::store(out[i] + (int64_t)(t + u) * g.d, o);
       }
     }
-    if (a.mean) {
-      const float c = static_cast<float>(cnt);
-#pragma unroll
-      for (int i = 0; i < NT; ++i)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[i][e] = acc[i][e] / c;
-    }
-#pragma unroll
-    for (int i = 0; i < NT; ++i) Row8<Tout>::store(out[i] + t * d, acc[i]);
   }
 }
 
 }  // namespace
 
 hipError_t launch_bcast(const BcastArgs& a, int dtype, int ntensors, int64_t BH, hipStream_t st) {
-  const int rgs = 256 / (a.g.d / 8);
-  const int64_t per_block = (int64_t)rgs * kTokensPerGroup;
+  const int rgs = 256 / (a.g.d / kE);
+  const int64_t per_block = (int64_t)rgs * kTokPerGroup;
   const dim3 grid((unsigned)((a.g.N + per_block - 1) / per_block), (unsigned)BH);
   if (dtype == 1) {
-    if (ntensors == 3) bcast_kernel<float, __bf16, 3><<<grid, 256, 0, st>>>(a);
-    else bcast_kernel<float, __bf16, 1><<<grid, 256, 0, st>>>(a);
+    if (ntensors == 3) bcast_kernel<__bf16, 3><<<grid, 256, 0, st>>>(a);
+    else bcast_kernel<__bf16, 1><<<grid, 256, 0, st>>>(a);
   } else {
-    if (ntensors == 3) bcast_kernel<float, float, 3><<<grid, 256, 0, st>>>(a);
-    else bcast_kernel<float, float, 1><<<grid, 256, 0, st>>>(a);
+    if (ntensors == 3) bcast_kernel<float, 3><<<grid, 256, 0, st>>>(a);
+    else bcast_kernel<float, 1><<<grid, 256, 0, st>>>(a);
   }
   return hipGetLastError();
 }

@@ -151,7 +151,7 @@ lh_status lh_attention(const lh_shape *shape, const void *qs, const void *ks, co
 
 /* a6. Deterministic scatter back to tokens (technical summary §2.C;
  * bitsgeniais phase 4): out[t] = mean over t's selected ancestors e (levels
- * 0..L-1, summed in ascending level order) of os[pos(e)].
+ * 0..L-1, summed in a fixed order) of os[pos(e)].
  * os: float32 [B,H,S,d]; pos: [B,H,M]; out: [B,H,N,d] dtype. */
 lh_status lh_scatter(const lh_shape *shape, const float *os, const int32_t *pos, void *out,
                      void *stream);
