@@ -234,6 +234,59 @@ def attention_rows(qs, ks, vs, rows):
     return out, lse
 
 
+def attention_block(qs, ks, vs, r0, r1):
+    """Rows r0..r1-1 of R10 attention (each row's softmax is independent, so
+    this is the same computation as `attention`, restricted to those rows)."""
+    S, d = qs.shape
+    tau = 1.0 / math.sqrt(d)
+    logits = (qs[r0:r1] @ ks[:r1].T) * tau
+    rows = np.arange(r0, r1)[:, None]
+    logits[np.arange(r1)[None, :] > rows] = -np.inf
+    m = logits.max(axis=1, keepdims=True)
+    e = np.exp(logits - m)
+    z = e.sum(axis=1, keepdims=True)
+    return (e / z) @ vs[:r1], (m + np.log(z))[:, 0]
+
+
+def attention_all_rows(qs, ks, vs, block=2048):
+    """(O, lse) of every row, computed `block` rows at a time (bounded memory)."""
+    S, d = qs.shape
+    O = np.zeros((S, d))
+    lse = np.zeros(S)
+    for r0 in range(0, S, block):
+        r1 = min(S, r0 + block)
+        O[r0:r1], lse[r0:r1] = attention_block(qs, ks, vs, r0, r1)
+    return O, lse
+
+
+def attention_backward_rows(qs, ks, vs, dos, lse, D, rows):
+    """dQ rows of R10 attention: dQ_i = tau * sum_{j<=i} P_ij (dP_ij - D_i) K_j
+    with P_ij = exp(tau q_i.k_j - lse_i), dP_ij = dO_i.v_j, D_i = dO_i.O_i."""
+    S, d = qs.shape
+    tau = 1.0 / math.sqrt(d)
+    out = np.zeros((len(rows), d))
+    for n, i in enumerate(rows):
+        P = np.exp((ks[: i + 1] @ qs[i]) * tau - lse[i])
+        dP = vs[: i + 1] @ dos[i]
+        out[n] = tau * (P * (dP - D[i])) @ ks[: i + 1]
+    return out
+
+
+def attention_backward_cols(qs, ks, vs, dos, lse, D, cols):
+    """dK and dV rows for key positions `cols`:
+    dV_j = sum_{i>=j} P_ij dO_i, dK_j = tau * sum_{i>=j} P_ij (dP_ij - D_i) Q_i."""
+    S, d = qs.shape
+    tau = 1.0 / math.sqrt(d)
+    dk = np.zeros((len(cols), d))
+    dv = np.zeros((len(cols), d))
+    for n, j in enumerate(cols):
+        P = np.exp((qs[j:] @ ks[j]) * tau - lse[j:])
+        dP = dos[j:] @ vs[j]
+        dv[n] = P @ dos[j:]
+        dk[n] = tau * (P * (dP - D[j:])) @ qs[j:]
+    return dk, dv
+
+
 # ----------------------------------------------------------------------------
 # stage 6: deterministic scatter back to tokens
 # [TS-es 2.C "Dispersión hacia atrás"], [BG phase 4], [TS-ja 2.C]
@@ -249,6 +302,17 @@ def contributors(pos: np.ndarray, N: int, p: int, L: int) -> np.ndarray:
     return c
 
 
+def ancestors(t: int, pos: np.ndarray, N: int, p: int, L: int):
+    """[(level, subsequence position)] of token t's selected ancestors, level 0 first."""
+    bases = level_bases(N, p, L)
+    out = []
+    for l in range(L):
+        r = int(pos[bases[l] + t // p ** l])
+        if r >= 0:
+            out.append((l, r))
+    return out
+
+
 def scatter(os_: np.ndarray, pos: np.ndarray, N: int, p: int, L: int) -> np.ndarray:
     """out[t] = mean over t's selected ancestors e of O_sub[pos(e)] (R11)."""
     bases = level_bases(N, p, L)
@@ -261,6 +325,31 @@ def scatter(os_: np.ndarray, pos: np.ndarray, N: int, p: int, L: int) -> np.ndar
         acc[hit] += os_[r[hit]]
         cnt += hit
     return acc / cnt[:, None]
+
+
+# ----------------------------------------------------------------------------
+# selection only (scores, top-K, causal order) and pooled rows on demand
+
+
+def select_head(q, k, p: int, L: int, S: int, dtype: str):
+    """score, sel, sub_idx, pos of one head (no attention)."""
+    N = q.shape[0]
+    score = scores(to_f64(q, dtype).astype(np.float32), to_f64(k, dtype).astype(np.float32), p, L)
+    sel = topk(score, N, p, L, S)
+    sub_idx, pos = causal_order(sel, N, p, L)
+    return dict(score=score, sel=sel, sub_idx=sub_idx, pos=pos)
+
+
+def pooled_rows(x64: np.ndarray, flat: np.ndarray, p: int, L: int, dtype: str) -> np.ndarray:
+    """Stored rows (rounded to dtype, as float64) of entries `flat`: level-0
+    tokens as given, level-l entries as the mean of their p**l tokens (R3)."""
+    N, d = x64.shape
+    lev, j = entry_of_flat(np.asarray(flat), N, p, L)
+    out = np.zeros((len(lev), d))
+    for n, (a, b) in enumerate(zip(lev, j)):
+        span = p ** int(a)
+        out[n] = x64[b * span:(b + 1) * span].mean(axis=0)
+    return to_f64(round_to(out, dtype), dtype)
 
 
 # ----------------------------------------------------------------------------
@@ -343,15 +432,23 @@ def pool_backward(dxs, pos, N, p, L):
     return acc
 
 
-def backward_head(dout, fwd: dict, p: int, L: int, dtype: str):
-    """(dq, dk, dv) float64 [N, d] of one head, from the stored forward."""
+def backward_stages(dout, fwd: dict, p: int, L: int, dtype: str) -> dict:
+    """Every intermediate of the backward of one head, float64:
+    dos (scatter backward), dqs/dks/dvs (attention backward), dq/dk/dv."""
     pos, sub_idx = fwd["pos"], fwd["sub_idx"]
     S = len(sub_idx)
     N = len(dout)
     qs, ks, vs = (to_f64(fwd[n], dtype) for n in ("qs", "ks", "vs"))
     dos = scatter_backward(to_f64(dout, dtype), pos, S, N, p, L)
     dqs, dks, dvs = attention_backward(qs, ks, vs, dos)
-    return tuple(pool_backward(x, pos, N, p, L) for x in (dqs, dks, dvs))
+    dq, dk, dv = (pool_backward(x, pos, N, p, L) for x in (dqs, dks, dvs))
+    return dict(dos=dos, dqs=dqs, dks=dks, dvs=dvs, dq=dq, dk=dk, dv=dv)
+
+
+def backward_head(dout, fwd: dict, p: int, L: int, dtype: str):
+    """(dq, dk, dv) float64 [N, d] of one head, from the stored forward."""
+    st = backward_stages(dout, fwd, p, L, dtype)
+    return st["dq"], st["dk"], st["dv"]
 
 
 # ----------------------------------------------------------------------------

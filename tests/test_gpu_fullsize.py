@@ -1,0 +1,107 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration the
+benchmark times (lh_forward / lh_backward on all heads).
+
+The oracle recomputes sampled parts one by one from the synthetic inputs:
+  * selection of a sampled head in full (scores, top-K, order, maps):
+    bit-exact;
+  * pooled rows at sampled entries and every gathered subsequence row;
+  * attention output and lse at sampled query rows;
+  * layer output at sampled tokens (mean over their ancestors' rows);
+  * gradients at sampled tokens: the oracle's exact lse and rowsum(dO*O) for
+    every row, then dQ at the ancestors' rows and dK, dV at their columns.
+Float bars as elsewhere (bf16: max|g-r| / max|r| <= 2e-2 over the sample;
+fp32: max-abs <= 1e-4).
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import lighthouse as O
+from synth import inputs as synth
+from tests.helpers import check_close, to_f64
+
+pytestmark = pytest.mark.gpu
+
+WORKLOADS = ["fwd_n4k_fp32", "fwd_n32k_bf16", "dense_n2k_bf16", "train_n98k_bf16",
+             "long_n512k_bf16", "long_n1m_bf16"]
+
+
+def sample_heads(cfg):
+    if cfg.N >= 1 << 20:
+        return [(0, cfg.H // 2)]
+    return [(0, 0), (0, cfg.H - 1)]
+
+
+def to_dev(a, dtype):
+    if dtype == "bf16":
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(a).cuda()
+
+
+@pytest.mark.parametrize("name", WORKLOADS)
+def test_full_size(name, gpu_lib):
+    from hierarchical_sparse_attention_pyramid_amd import binding as lb
+    cfg = synth.CONFIGS[name]
+    B, H, N, d, p, L, S, dt = cfg.B, cfg.H, cfg.N, cfg.d, cfg.p, cfg.L, cfg.S, cfg.dtype
+    print(f"[gpu-fullsize] {name}: drawing inputs", flush=True)
+    names = ("q", "k", "v", "dout") if cfg.backward else ("q", "k", "v")
+    host = synth.make_inputs(cfg, tensors=names)
+    dev = {n: to_dev(host[n], dt) for n in names}
+    print(f"[gpu-fullsize] {name}: GPU forward{'+backward' if cfg.backward else ''}", flush=True)
+    out, bufs, shape = lb.forward(dev["q"], dev["k"], dev["v"], p, L, S)
+    if cfg.backward:
+        dq, dk, dv = lb.backward(shape, dev["dout"], bufs)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(4242)
+    for b, h in sample_heads(cfg):
+        print(f"[gpu-fullsize] {name}: oracle on head ({b},{h})", flush=True)
+        x64 = {n: O.to_f64(host[n][b, h], dt) for n in names}
+        sel = O.select_head(host["q"][b, h], host["k"][b, h], p, L, S, dt)
+        got_score = bufs.score[b, h].cpu().numpy()
+        assert np.array_equal(got_score.view(np.uint32), sel["score"].view(np.uint32)), "scores differ"
+        for key in ("sel", "sub_idx", "pos"):
+            np.testing.assert_array_equal(getattr(bufs, key)[b, h].cpu().numpy(), sel[key])
+        pos, sub_idx = sel["pos"], sel["sub_idx"]
+        M = len(pos)
+        # pooled rows at sampled entries of every level >= 1
+        if M > N:
+            ent = np.sort(rng.choice(np.arange(N, M), min(256, M - N), replace=False))
+            for src, pyr in (("q", bufs.pq), ("k", bufs.pk), ("v", bufs.pv)):
+                ref = O.pooled_rows(x64[src], ent, p, L, dt)
+                check_close(to_f64(pyr[b, h][torch.from_numpy(ent - N).cuda()]), ref, dt, f"p{src}")
+        # every gathered row
+        orow = {n: O.pooled_rows(x64[n], sub_idx, p, L, dt) for n in ("q", "k", "v")}
+        for n, t in (("q", bufs.qs), ("k", bufs.ks), ("v", bufs.vs)):
+            check_close(to_f64(t[b, h]), orow[n], dt, f"{n}s")
+        # sampled tokens and the subsequence rows they need
+        toks = [0, N - 1] + rng.choice(N, 40, replace=False).tolist()
+        if cfg.planted:
+            toks += synth.planted_positions(cfg.seed, N)[:8].tolist()
+        toks = sorted(set(toks))
+        anc = {t: O.ancestors(t, pos, N, p, L) for t in toks}
+        need = sorted({r for t in toks for _, r in anc[t]})
+        rows = sorted(set(need) | {0, S - 1} | set(rng.choice(S, 24, replace=False).tolist()))
+        o_rows, lse_rows = O.attention_rows(orow["q"], orow["k"], orow["v"], rows)
+        idx = torch.tensor(rows).cuda()
+        check_close(to_f64(bufs.os[b, h][idx]), o_rows, dt, "os rows")
+        check_close(to_f64(bufs.lse[b, h][idx]), lse_rows, dt, "lse rows")
+        o_of = dict(zip(rows, o_rows))
+        ref_out = np.stack([np.mean([o_of[r] for _, r in anc[t]], axis=0) for t in toks])
+        tix = torch.tensor(toks).cuda()
+        check_close(to_f64(out[b, h][tix]), ref_out, dt, "out tokens")
+        if not cfg.backward:
+            continue
+        print(f"[gpu-fullsize] {name}: oracle backward on head ({b},{h})", flush=True)
+        dos = O.scatter_backward(x64["dout"], pos, S, N, p, L)
+        O_all, lse_all = O.attention_all_rows(orow["q"], orow["k"], orow["v"])
+        D = (dos * O_all).sum(axis=1)
+        dqs = O.attention_backward_rows(orow["q"], orow["k"], orow["v"], dos, lse_all, D, need)
+        dks, dvs = O.attention_backward_cols(orow["q"], orow["k"], orow["v"], dos, lse_all, D, need)
+        at = {r: n for n, r in enumerate(need)}
+        for got, src in ((dq, dqs), (dk, dks), (dv, dvs)):
+            ref = np.stack([sum(src[at[r]] / p ** l for l, r in anc[t]) for t in toks])
+            check_close(to_f64(got[b, h][tix]), ref, dt, "grad tokens")
+    del dev, out, bufs
+    torch.cuda.empty_cache()

@@ -311,3 +311,43 @@ def test_every_token_gets_gradient():
     f = O.forward_head(q, k, v, p, L, 4 + 3, "f64")
     dq, dk, dv = O.backward_head(dout, f, p, L, "f64")
     assert np.all(np.abs(dv).sum(1) > 0)
+
+
+# ---------------------------------------------------------------- sampled forms
+
+def test_row_and_column_forms_match_full_attention():
+    """The per-row / per-column evaluations used at full sizes agree with the
+    whole-matrix forms (which are pinned above against torch and closed forms)."""
+    r = rng(14)
+    S, d = 90, 16
+    q, k, v, g = (r.standard_normal((S, d)) for _ in range(4))
+    o, lse = O.attention(q, k, v)
+    o2, lse2 = O.attention_all_rows(q, k, v, block=32)
+    np.testing.assert_allclose(o2, o, atol=1e-12)
+    np.testing.assert_allclose(lse2, lse, atol=1e-12)
+    dq, dk, dv = O.attention_backward(q, k, v, g)
+    D = (g * o).sum(axis=1)
+    rows = [0, 1, 45, 89]
+    np.testing.assert_allclose(O.attention_backward_rows(q, k, v, g, lse, D, rows), dq[rows], atol=1e-10)
+    dk2, dv2 = O.attention_backward_cols(q, k, v, g, lse, D, rows)
+    np.testing.assert_allclose(dk2, dk[rows], atol=1e-10)
+    np.testing.assert_allclose(dv2, dv[rows], atol=1e-10)
+
+
+def test_selection_and_pooled_rows_forms_match_forward():
+    from synth import bf16_bits_from_f32
+    r = rng(15)
+    N, d, p, L, S = 256, 16, 4, 4, 30
+    q, k, v = (bf16_bits_from_f32(r.standard_normal((N, d)).astype(np.float32)) for _ in range(3))
+    f = O.forward_head(q, k, v, p, L, S, "bf16")
+    sel = O.select_head(q, k, p, L, S, "bf16")
+    for key in ("score", "sel", "sub_idx", "pos"):
+        np.testing.assert_array_equal(sel[key], f[key])
+    rows = O.pooled_rows(O.to_f64(q, "bf16"), f["sub_idx"], p, L, "bf16")
+    np.testing.assert_array_equal(rows, O.to_f64(f["qs"], "bf16"))
+    c = O.contributors(f["pos"], N, p, L)
+    for t in (0, 5, 255):
+        anc = O.ancestors(t, f["pos"], N, p, L)
+        assert len(anc) == c[t]
+        o = np.mean([O.to_f64(f["os"], "fp32")[pos] for _, pos in anc], axis=0)
+        np.testing.assert_allclose(o, O.to_f64(f["out"], "bf16")[t], rtol=2 ** -7, atol=1e-6)
