@@ -41,9 +41,11 @@
 #define LH_BKV64_MINW 2
 #define LH_BKV128_WAVES 8
 #define LH_BKV128_MINW 1
+#define LH_BKV128_VLDS 1
 #define LH_BQ64_WAVES 4
 #define LH_BQ128_WAVES 8
-#define LH_BQ_MINW 2
+#define LH_BQ64_MINW 2
+#define LH_BQ128_MINW 2
 #endif
 
 namespace lh {
@@ -260,33 +262,43 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void attn_fwd_bf16(
     for (int qb = 0; qb < NQB; ++qb) {
       const int qbase = qw0 + qb * 32;
       if (k0 > qbase + 31) continue;
+      // Issue every LDS read of this step before the first MFMA that needs
+      // it: the V^T operands do not depend on the scores, so their latency
+      // hides under the QK^T products and the softmax.
+      bf16x8 kop[2][D / 16];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int dc = 0; dc < D / 16; ++dc) kop[kb][dc] = rd_rows<D>(sK, kb * 32 + c32, 2 * dc + h);
+      bf16x8 vop[2][2][D / 32];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+          for (int mb = 0; mb < D / 32; ++mb)
+            vop[kb][c][mb] = rd_tr8<D>(sV, kb * 32 + 16 * c + 4 * h, mb * 32, lane);
       f32x16 sacc[2] = {zero16(), zero16()};
 #pragma unroll
       for (int dc = 0; dc < D / 16; ++dc)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-          sacc[kb] = mfma32(rd_rows<D>(sK, kb * 32 + c32, 2 * dc + h), qreg[qb][dc], sacc[kb]);
+        for (int kb = 0; kb < 2; ++kb) sacc[kb] = mfma32(kop[kb][dc], qreg[qb][dc], sacc[kb]);
       const int query = qbase + c32;
-      float mx = neg_inf();
+      float mx = neg_inf();   // max of raw scores (the scale is positive)
       if (k0 + C::kKT - 1 > qbase) {  // diagonal tile: causal mask
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int key = k0 + kb * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
-            sacc[kb][i] = key > query ? neg_inf() : sacc[kb][i] * sl2;
-            mx = fmaxf(mx, sacc[kb][i]);
-          }
-      } else {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            sacc[kb][i] *= sl2;
-            mx = fmaxf(mx, sacc[kb][i]);
+            if (key > query) sacc[kb][i] = neg_inf();
           }
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
       if (__any(mx > mrow[qb] + kLazyRescale)) {  // wave-uniform
         const float mnew = fmaxf(mrow[qb], mx);
         const float alpha = fexp2(mrow[qb] - mnew);
@@ -295,7 +307,7 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void attn_fwd_bf16(
         for (int mb = 0; mb < D / 32; ++mb) oacc[qb][mb] *= alpha;
         mrow[qb] = mnew;
       }
-      const float m = mrow[qb];
+      const float nm = -mrow[qb];
       bf16x8 pk[2][2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -303,7 +315,7 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void attn_fwd_bf16(
         for (int c = 0; c < 2; ++c)
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            const float pv = fexp2(sacc[kb][8 * c + e] - m);
+            const float pv = fexp2(__builtin_fmaf(sacc[kb][8 * c + e], sl2, nm));
             lsum[qb] += pv;
             pk[kb][c][e] = static_cast<__bf16>(pv);
           }
@@ -313,8 +325,7 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void attn_fwd_bf16(
         for (int c = 0; c < 2; ++c)
 #pragma unroll
           for (int mb = 0; mb < D / 32; ++mb)
-            oacc[qb][mb] = mfma32(rd_tr8<D>(sV, kb * 32 + 16 * c + 4 * h, mb * 32, lane),
-                                  pk[kb][c], oacc[qb][mb]);
+            oacc[qb][mb] = mfma32(vop[kb][c][mb], pk[kb][c], oacc[qb][mb]);
     }
   }
 
@@ -392,7 +403,11 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void attn_bwd_dkdv_bf16(
     const __bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ DELTA,
     float* __restrict__ dK, float* __restrict__ dV, int S, float sl2, float scale) {
   using C = BwdKVCfg<D, WAVES>;
+  // d = 128: the wave's 32 V rows live in LDS instead of registers (the
+  // register file would otherwise spill); they are the B operand of dP.
+  constexpr bool kVInLds = D == 128 && LH_BKV128_VLDS;
   __shared__ __attribute__((aligned(1024))) __bf16 sT[2][2][C::kTile];  // [buffer][Q, dO]
+  __shared__ __attribute__((aligned(1024))) __bf16 sVw[kVInLds ? WAVES : 1][kVInLds ? 32 * D : 8];
   __shared__ float sLD[2][2][C::kQT];                                  // [buffer][lse, delta]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, c32 = lane & 31;
@@ -418,11 +433,16 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void attn_bwd_dkdv_bf16(
   };
   issue(t0, 0);
 
-  bf16x8 kreg[D / 16], vreg[D / 16];
+  bf16x8 kreg[D / 16], vreg[kVInLds ? 1 : D / 16];
 #pragma unroll
-  for (int dc = 0; dc < D / 16; ++dc) {
+  for (int dc = 0; dc < D / 16; ++dc)
     kreg[dc] = key < S ? *reinterpret_cast<const bf16x8*>(K + off + (int64_t)key * D + dc * 16 + 8 * h) : zero8();
-    vreg[dc] = key < S ? *reinterpret_cast<const bf16x8*>(V + off + (int64_t)key * D + dc * 16 + 8 * h) : zero8();
+  if constexpr (kVInLds) {
+    load_tile<D, 32, 1>(V + off, S, kw0, sVw[wave], 0, lane);  // landed by the first barrier
+  } else {
+#pragma unroll
+    for (int dc = 0; dc < D / 16; ++dc)
+      vreg[dc] = key < S ? *reinterpret_cast<const bf16x8*>(V + off + (int64_t)key * D + dc * 16 + 8 * h) : zero8();
   }
   f32x16 dka[D / 32], dva[D / 32];
 #pragma unroll
@@ -450,7 +470,8 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void attn_bwd_dkdv_bf16(
 #pragma unroll
       for (int dc = 0; dc < D / 16; ++dc) {
         sacc = mfma32(rd_rows<D>(sQ, qs * 32 + c32, 2 * dc + h), kreg[dc], sacc);
-        dpacc = mfma32(rd_rows<D>(sG, qs * 32 + c32, 2 * dc + h), vreg[dc], dpacc);
+        const bf16x8 vb = kVInLds ? rd_rows<D>(sVw[wave], c32, 2 * dc + h) : vreg[kVInLds ? 0 : dc];
+        dpacc = mfma32(rd_rows<D>(sG, qs * 32 + c32, 2 * dc + h), vb, dpacc);
       }
       const bool diag = qbase < kw0 + 31;
       bf16x8 pch[2], dsch[2];
@@ -663,12 +684,12 @@ hipError_t launch_attn_bwd(const void* q, const void* k, const void* v, const fl
   if (d == 64) {
     using C2 = BwdQCfg<64, LH_BQ64_WAVES>;
     const dim3 g2((unsigned)((S + C2::kQB - 1) / C2::kQB * BH));
-    attn_bwd_dq_bf16<64, LH_BQ64_WAVES, LH_BQ_MINW><<<g2, 64 * LH_BQ64_WAVES, 0, st>>>(
+    attn_bwd_dq_bf16<64, LH_BQ64_WAVES, LH_BQ64_MINW><<<g2, 64 * LH_BQ64_WAVES, 0, st>>>(
         Q, K, V, G, lse, delta, dq, (int)S, sl2, scale);
   } else {
     using C2 = BwdQCfg<128, LH_BQ128_WAVES>;
     const dim3 g2((unsigned)((S + C2::kQB - 1) / C2::kQB * BH));
-    attn_bwd_dq_bf16<128, LH_BQ128_WAVES, LH_BQ_MINW><<<g2, 64 * LH_BQ128_WAVES, 0, st>>>(
+    attn_bwd_dq_bf16<128, LH_BQ128_WAVES, LH_BQ128_MINW><<<g2, 64 * LH_BQ128_WAVES, 0, st>>>(
         Q, K, V, G, lse, delta, dq, (int)S, sl2, scale);
   }
   e = hipGetLastError();
