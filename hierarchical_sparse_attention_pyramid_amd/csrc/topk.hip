@@ -16,7 +16,11 @@
 //
 // Workspace per head (uint32): [0] threshold prefix, [1] remaining count,
 // [2..3] unused, [4..4+2048) histogram, then four arrays of nblk block
-// counters (greater, equal, output offset, equal-before).
+// counters (greater, equal, output offset, equal-before).  The serial steps
+// (bin pick, block-offset scan) are separate one-block-per-head launches: a
+// "last block finishes the pass" scheme would need a device-scope fence in
+// every block, which on a multi-XCD GPU (one L2 per XCD) costs more than a
+// launch.
 #include "kernels.h"
 
 namespace lh {
@@ -40,33 +44,9 @@ __global__ __launch_bounds__(kThreads) void topk_init(void* ws, int64_t nblk, in
   uint32_t* w = head_ws(ws, blockIdx.x, nblk);
   for (int b = threadIdx.x; b < kBins; b += kThreads) w[4 + b] = 0;
   if (threadIdx.x == 0) {
-    w[0] = 0;
-    w[1] = (uint32_t)K;
+    w[0] = 0;           // threshold prefix
+    w[1] = (uint32_t)K; // candidates still to take at or below the prefix
   }
-}
-
-__global__ __launch_bounds__(kThreads) void topk_hist(const float* score, void* ws, int64_t nblk,
-                                                      int32_t M, int32_t C, int pass) {
-  __shared__ uint32_t h[kBins];
-  const int64_t bh = blockIdx.y;
-  uint32_t* w = head_ws(ws, bh, nblk);
-  int shift, nbits;
-  pass_bits(pass, shift, nbits);
-  const uint32_t mask = (1u << nbits) - 1u;
-  const int hi = shift + nbits;
-  for (int b = threadIdx.x; b < kBins; b += kThreads) h[b] = 0;
-  __syncthreads();
-  const uint32_t prefix = w[0];
-  const float* s = score + bh * M;
-  const int i0 = blockIdx.x * kSlice;
-  const int i1 = min(i0 + kSlice, C);
-  for (int i = i0 + threadIdx.x; i < i1; i += kThreads) {
-    const uint32_t u = __float_as_uint(s[i]);
-    if (hi >= 32 || ((u ^ prefix) >> hi) == 0u) atomicAdd(&h[(u >> shift) & mask], 1u);
-  }
-  __syncthreads();
-  for (int b = threadIdx.x; b < kBins; b += kThreads)
-    if (h[b]) atomicAdd(&w[4 + b], h[b]);
 }
 
 // Exclusive prefix sum over the 256 threads of a block (in thread order).
@@ -91,6 +71,34 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* sh, ui
   return before + x - v;
 }
 
+// Histogram pass `pass` over this block's slice (LDS bins, then integer
+// atomics into the head's histogram).
+__global__ __launch_bounds__(kThreads) void topk_hist(const float* score, void* ws, int64_t nblk,
+                                                      int32_t M, int32_t C, int pass) {
+  __shared__ uint32_t h[kBins];
+  const int64_t bh = blockIdx.y;
+  uint32_t* w = head_ws(ws, bh, nblk);
+  int shift, nbits;
+  pass_bits(pass, shift, nbits);
+  const uint32_t mask = (1u << nbits) - 1u;
+  const int hi = shift + nbits;
+  for (int b = threadIdx.x; b < kBins; b += kThreads) h[b] = 0;
+  __syncthreads();
+  const uint32_t prefix = w[0];
+  const float* s = score + bh * M;
+  const int i0 = blockIdx.x * kSlice;
+  const int i1 = min(i0 + kSlice, C);
+  for (int i = i0 + threadIdx.x; i < i1; i += kThreads) {
+    const uint32_t u = __float_as_uint(s[i]);
+    if (hi >= 32 || ((u ^ prefix) >> hi) == 0u) atomicAdd(&h[(u >> shift) & mask], 1u);
+  }
+  __syncthreads();
+  for (int b = threadIdx.x; b < kBins; b += kThreads)
+    if (h[b]) atomicAdd(&w[4 + b], h[b]);
+}
+
+// One block per head: pick the bin holding the K-th candidate, narrow the
+// prefix, clear the histogram for the next pass.
 __global__ __launch_bounds__(kThreads) void topk_pick(void* ws, int64_t nblk, int pass) {
   __shared__ uint32_t sh[kThreads / 64];
   uint32_t* w = head_ws(ws, blockIdx.x, nblk);
@@ -122,6 +130,7 @@ __global__ __launch_bounds__(kThreads) void topk_pick(void* ws, int64_t nblk, in
   for (int b = threadIdx.x; b < kBins; b += kThreads) w[4 + b] = 0;
 }
 
+// Per-block counts of candidates above and equal to the threshold.
 __global__ __launch_bounds__(kThreads) void topk_count(const float* score, void* ws, int64_t nblk,
                                                        int32_t M, int32_t C) {
   __shared__ uint32_t sh[kThreads / 64];
@@ -147,20 +156,36 @@ __global__ __launch_bounds__(kThreads) void topk_count(const float* score, void*
   }
 }
 
-__global__ void topk_scan(void* ws, int64_t nblk) {
+// One block per head: output offset of every block (equal candidates are
+// taken in flat order until `need` of them are in).
+__global__ __launch_bounds__(kThreads) void topk_scan(void* ws, int64_t nblk) {
+  __shared__ uint32_t sh[kThreads / 64];
+  __shared__ uint32_t carry[2];
   uint32_t* w = head_ws(ws, blockIdx.x, nblk);
-  if (threadIdx.x != 0) return;
-  const uint32_t need = w[1];
   uint32_t* blk = w + 4 + kBins;
-  uint32_t off = 0, eqb = 0;
-  for (int64_t b = 0; b < nblk; ++b) {
-    const uint32_t gt = blk[b], eq = blk[nblk + b];
+  const uint32_t need = w[1];
+  if (threadIdx.x == 0) carry[0] = carry[1] = 0;
+  __syncthreads();
+  for (int64_t b0 = 0; b0 < nblk; b0 += kThreads) {
+    const int64_t b = b0 + threadIdx.x;
+    const uint32_t g1 = b < nblk ? blk[b] : 0u;
+    const uint32_t e1 = b < nblk ? blk[nblk + b] : 0u;
+    uint32_t etot;
+    const uint32_t eqb = carry[1] + block_excl_scan(e1, sh, etot);
     const uint32_t left = need > eqb ? need - eqb : 0u;
-    const uint32_t take = eq < left ? eq : left;
-    blk[2 * nblk + b] = off;
-    blk[3 * nblk + b] = eqb;
-    off += gt + take;
-    eqb += eq;
+    const uint32_t take = e1 < left ? e1 : left;
+    uint32_t otot;
+    const uint32_t off = carry[0] + block_excl_scan(g1 + take, sh, otot);
+    if (b < nblk) {
+      blk[2 * nblk + b] = off;
+      blk[3 * nblk + b] = eqb;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      carry[0] += otot;
+      carry[1] += etot;
+    }
+    __syncthreads();
   }
 }
 
@@ -214,7 +239,7 @@ hipError_t launch_topk(const float* score, int32_t* sel, void* ws, const Geo& g,
     topk_pick<<<(unsigned)BH, kThreads, 0, st>>>(ws, nblk, pass);
   }
   topk_count<<<grid, kThreads, 0, st>>>(score, ws, nblk, g.M, g.C);
-  topk_scan<<<(unsigned)BH, 64, 0, st>>>(ws, nblk);
+  topk_scan<<<(unsigned)BH, kThreads, 0, st>>>(ws, nblk);
   topk_write<<<grid, kThreads, 0, st>>>(score, sel, ws, nblk, g.M, g.C, g.K);
   return hipGetLastError();
 }
