@@ -48,6 +48,21 @@
 #define LH_BQ128_MINW 2
 #endif
 
+// Causal pairing per pass (measured: it pays where a launch has few, long
+// workgroups; with d = 64 the extra resident waves of the unpaired grid win).
+#ifndef LH_PAIR_FWD
+#define LH_PAIR_FWD 0
+#endif
+#ifndef LH_PAIR_BKV64
+#define LH_PAIR_BKV64 0
+#endif
+#ifndef LH_PAIR_BKV128
+#define LH_PAIR_BKV128 1
+#endif
+#ifndef LH_PAIR_BQ
+#define LH_PAIR_BQ 0
+#endif
+
 namespace lh {
 
 namespace {
@@ -66,6 +81,23 @@ __device__ __forceinline__ bf16x8 zero8() {
 #pragma unroll
   for (int e = 0; e < 8; ++e) z[e] = static_cast<__bf16>(0.f);
   return z;
+}
+
+// max over lanes l and l ^ 32 (the two halves of a query column)
+__device__ __forceinline__ float max_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+
+// acc + the sum of the eight bf16 values of v (two-element dot products with 1)
+__device__ __forceinline__ float add_bf16x8(const bf16x8& v, float acc) {
+  const bf16x2 one = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 0, 1), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 2, 3), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 4, 5), one, acc, false);
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 6, 7), one, acc, false);
 }
 
 __device__ __forceinline__ f32x16 zero16() {
@@ -179,6 +211,51 @@ __device__ __forceinline__ void map_block(int p, int T, int BH, int nqb, int& he
   (void)T;
 }
 
+// Causal pairing: block b costs in proportion to b + 1 (or to nb - b for key
+// blocks), so a workgroup that runs blocks r and nb - 1 - r back to back does
+// the same work as every other one.  Without pairing the heaviest blocks set
+// the kernel's length while the light ones leave compute units idle at the
+// end.  Small grids are not paired (halving them would leave units idle).
+// Returns the workgroup's head and its one or two blocks in run order
+// (`rank` counts from the heavy end: block nb - 1 - rank for query blocks).
+struct Runs {
+  int head, n, rank[2];
+};
+
+__device__ __forceinline__ Runs plan_runs(int p, int T, int nb, int paired) {
+  Runs r;
+  if (!paired) {
+    int qblk;
+    map_block(p, T, T / nb, nb, r.head, qblk);
+    r.n = 1;
+    r.rank[0] = nb - 1 - qblk;
+    r.rank[1] = 0;
+    return r;
+  }
+  const int np = (nb + 1) / 2;
+  const int BH = T / np;
+  int pair;
+  if ((BH & 7) == 0) {
+    const int x = p & 7, local = p >> 3, hpx = BH >> 3;
+    r.head = x * hpx + local % hpx;
+    pair = local / hpx;
+  } else {
+    r.head = p % BH;
+    pair = p / BH;
+  }
+  r.rank[0] = pair;            // heavy: rank pair from the heavy end
+  r.rank[1] = nb - 1 - pair;   // light partner
+  r.n = r.rank[1] > r.rank[0] ? 2 : 1;
+  return r;
+}
+
+// Number of workgroups of a (possibly paired) causal grid.
+inline int64_t causal_grid(int64_t nb, int64_t BH, bool paired) {
+  return (paired ? (nb + 1) / 2 : nb) * BH;
+}
+
+inline bool pair_blocks(int64_t nb, int64_t BH) { return nb * BH >= 1024 && nb >= 2; }
+
 // ------------------------------------------------------------------ forward
 //
 // Online softmax with lazy rescaling: a row keeps its running maximum m
@@ -204,16 +281,18 @@ struct FwdCfg {
 template <int D, int QW, int WAVES, int MINW>
 __global__ __launch_bounds__(64 * WAVES, MINW) void attn_fwd_bf16(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
-    float* __restrict__ O, float* __restrict__ LSE, int S, float sl2) {
+    float* __restrict__ O, float* __restrict__ LSE, int S, float sl2, int paired) {
   using C = FwdCfg<D, QW, WAVES>;
   constexpr int NQB = C::kNQB;
   __shared__ __attribute__((aligned(1024))) __bf16 sKV[2][2][C::kTile];  // [buffer][K,V]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, c32 = lane & 31;
   const int nqb = (S + C::kQB - 1) / C::kQB;
-  int head, qblk;
-  map_block(blockIdx.x, gridDim.x, gridDim.x / nqb, nqb, head, qblk);
-  const int64_t bh = head;
+  const Runs runs = plan_runs(blockIdx.x, gridDim.x, nqb, paired);
+  const int64_t bh = runs.head;
+  for (int run = 0; run < runs.n; ++run) {
+  if (run > 0) __syncthreads();  // every wave is done with the LDS tiles
+  const int qblk = nqb - 1 - runs.rank[run];
   const int q0 = qblk * C::kQB;
   const int qw0 = q0 + wave * C::kQW;
   const __bf16* Qh = Q + bh * (int64_t)S * D;
@@ -298,9 +377,11 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void attn_fwd_bf16(
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
+      // This lane's half of the tile; the running maximum is shared by both
+      // halves, so the exact column maximum is needed only to rescale.
+      mx *= sl2;
       if (__any(mx > mrow[qb] + kLazyRescale)) {  // wave-uniform
-        const float mnew = fmaxf(mrow[qb], mx);
+        const float mnew = fmaxf(mrow[qb], max_halves(mx));
         const float alpha = fexp2(mrow[qb] - mnew);
         lsum[qb] *= alpha;
 #pragma unroll
@@ -312,13 +393,13 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void attn_fwd_bf16(
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int c = 0; c < 2; ++c)
+        for (int c = 0; c < 2; ++c) {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float pv = fexp2(__builtin_fmaf(sacc[kb][8 * c + e], sl2, nm));
-            lsum[qb] += pv;
-            pk[kb][c][e] = static_cast<__bf16>(pv);
-          }
+          for (int e = 0; e < 8; ++e)
+            pk[kb][c][e] = static_cast<__bf16>(fexp2(__builtin_fmaf(sacc[kb][8 * c + e], sl2, nm)));
+          // the normaliser sums the rounded weights the products use
+          lsum[qb] = add_bf16x8(pk[kb][c], lsum[qb]);
+        }
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -329,27 +410,29 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void attn_fwd_bf16(
     }
   }
 
-  if (qw0 >= S) return;
-  float* Oh = O + bh * (int64_t)S * D;
-  float* Lh = LSE + bh * (int64_t)S;
+  if (qw0 < S) {
+    float* Oh = O + bh * (int64_t)S * D;
+    float* Lh = LSE + bh * (int64_t)S;
 #pragma unroll
-  for (int qb = 0; qb < NQB; ++qb) {
-    const float lt = lsum[qb] + __shfl_xor(lsum[qb], 32);
-    const float inv = 1.0f / lt;
-    const int query = qw0 + qb * 32 + c32;
-    if (query < S) {
+    for (int qb = 0; qb < NQB; ++qb) {
+      const float lt = lsum[qb] + __shfl_xor(lsum[qb], 32);
+      const float inv = 1.0f / lt;
+      const int query = qw0 + qb * 32 + c32;
+      if (query < S) {
 #pragma unroll
-      for (int mb = 0; mb < D / 32; ++mb)
+        for (int mb = 0; mb < D / 32; ++mb)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          f32x4 o;
+          for (int j = 0; j < 4; ++j) {
+            f32x4 o;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) o[r] = oacc[qb][mb][4 * j + r] * inv;
-          *reinterpret_cast<f32x4*>(Oh + (int64_t)query * D + mb * 32 + 8 * j + 4 * h) = o;
-        }
-      if (h == 0) Lh[query] = (mrow[qb] + log2f(lt)) * kLn2;
+            for (int r = 0; r < 4; ++r) o[r] = oacc[qb][mb][4 * j + r] * inv;
+            *reinterpret_cast<f32x4*>(Oh + (int64_t)query * D + mb * 32 + 8 * j + 4 * h) = o;
+          }
+        if (h == 0) Lh[query] = (mrow[qb] + log2f(lt)) * kLn2;
+      }
     }
   }
+  }  // run
 }
 
 // ------------------------------------------------------------------ backward
@@ -358,9 +441,12 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void attn_fwd_bf16(
 // O is the float32 forward output: rounding it to bf16 first would perturb
 // delta by ~2^-9 |dO||O|, and dS = P (dP - delta) cancels for keys that
 // dominate a row, which would amplify that error in dK and dQ.
+// It also writes lse * log2(e) (lse2), the form the bf16 passes use.
 template <typename T>
 __global__ __launch_bounds__(256) void attn_delta(const float* __restrict__ O, const T* __restrict__ dO,
-                                                  float* __restrict__ delta, int64_t rows, int d) {
+                                                  const float* __restrict__ LSE,
+                                                  float* __restrict__ delta, float* __restrict__ lse2,
+                                                  int64_t rows, int d) {
   const int lpr = d / 8;
   const int rgs = 256 / lpr;
   const int lane = threadIdx.x % lpr;
@@ -374,7 +460,10 @@ __global__ __launch_bounds__(256) void attn_delta(const float* __restrict__ O, c
     for (int e = 0; e < 8; ++e) s += o[e] * g[e];
   }
   for (int off = lpr >> 1; off >= 1; off >>= 1) s += __shfl_xor(s, off);
-  if (row < rows && lane == 0) delta[row] = s;
+  if (row < rows && lane == 0) {
+    delta[row] = s;
+    if (lse2) lse2[row] = LSE[row] * kLog2e;
+  }
 }
 
 // Stage 64 float32 values (lse or delta of a query tile) into LDS with one
@@ -397,11 +486,27 @@ struct BwdKVCfg {
   static constexpr int kTile = kQT * D;
 };
 
+// P and dS of a 32-query x 32-key slice in B-operand chunks (key column per
+// lane).  sL holds lse * log2(e), sD rowsum(dO*O) of the query tile.
+template <bool kMask>
+__device__ __forceinline__ void kv_weights(const f32x16& sacc, const f32x16& dpacc, const float* sL,
+                                           const float* sD, int qs, int h, float sl2, int key,
+                                           int q0, int S, bf16x8 (&pch)[2], bf16x8 (&dsch)[2]) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int qi = qs * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
+    float p = fexp2(__builtin_fmaf(sacc[i], sl2, -sL[qi]));
+    if (kMask && (key > q0 + qi || q0 + qi >= S)) p = 0.f;
+    pch[i >> 3][i & 7] = static_cast<__bf16>(p);
+    dsch[i >> 3][i & 7] = static_cast<__bf16>(p * (dpacc[i] - sD[qi]));
+  }
+}
+
 template <int D, int WAVES, int MINW>
 __global__ __launch_bounds__(64 * WAVES, MINW) void attn_bwd_dkdv_bf16(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
-    const __bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ DELTA,
-    float* __restrict__ dK, float* __restrict__ dV, int S, float sl2, float scale) {
+    const __bf16* __restrict__ dO, const float* __restrict__ LSE2, const float* __restrict__ DELTA,
+    float* __restrict__ dK, float* __restrict__ dV, int S, float sl2, float scale, int paired) {
   using C = BwdKVCfg<D, WAVES>;
   // d = 128: the wave's 32 V rows live in LDS instead of registers (the
   // register file would otherwise spill); they are the B operand of dP.
@@ -412,15 +517,16 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void attn_bwd_dkdv_bf16(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, c32 = lane & 31;
   const int nkb = (S + C::kKB - 1) / C::kKB;
-  int head, rank;
-  map_block(blockIdx.x, gridDim.x, gridDim.x / nkb, nkb, head, rank);
-  const int kblk = nkb - 1 - rank;  // early keys (most queries) first
-  const int64_t bh = head;
+  const Runs runs = plan_runs(blockIdx.x, gridDim.x, nkb, paired);
+  const int64_t bh = runs.head;
+  for (int run = 0; run < runs.n; ++run) {
+  if (run > 0) __syncthreads();  // every wave is done with the LDS tiles
+  const int kblk = runs.rank[run];  // early keys (most queries) are the heavy end
   const int kb0 = kblk * C::kKB;
   const int kw0 = kb0 + wave * C::kKW;
   const int key = kw0 + c32;
   const int64_t off = bh * (int64_t)S * D;
-  const float* lse_h = LSE + bh * (int64_t)S;
+  const float* lse_h = LSE2 + bh * (int64_t)S;
   const float* del_h = DELTA + bh * (int64_t)S;
 
   const int t0 = kb0 / C::kQT;
@@ -473,17 +579,13 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void attn_bwd_dkdv_bf16(
         const bf16x8 vb = kVInLds ? rd_rows<D>(sVw[wave], c32, 2 * dc + h) : vreg[kVInLds ? 0 : dc];
         dpacc = mfma32(rd_rows<D>(sG, qs * 32 + c32, 2 * dc + h), vb, dpacc);
       }
-      const bool diag = qbase < kw0 + 31;
+      // Only a slice that meets the diagonal or the end of the sequence needs
+      // masks (a wave-uniform branch keeps them off every other slice).
       bf16x8 pch[2], dsch[2];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int qi = qs * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
-        float p = fexp2(__builtin_fmaf(sacc[i], sl2, -sL[qi] * kLog2e));
-        if (diag && key > q0 + qi) p = 0.f;
-        if (q0 + qi >= S) p = 0.f;
-        pch[i >> 3][i & 7] = static_cast<__bf16>(p);
-        dsch[i >> 3][i & 7] = static_cast<__bf16>(p * (dpacc[i] - sD[qi]));
-      }
+      if (qbase < kw0 + 31 || q0 + C::kQT > S)
+        kv_weights<true>(sacc, dpacc, sL, sD, qs, h, sl2, key, q0, S, pch, dsch);
+      else
+        kv_weights<false>(sacc, dpacc, sL, sD, qs, h, sl2, key, q0, S, pch, dsch);
 #pragma unroll
       for (int c = 0; c < 2; ++c)
 #pragma unroll
@@ -494,21 +596,23 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void attn_bwd_dkdv_bf16(
         }
     }
   }
-  if (key >= S) return;
+  if (key < S) {
 #pragma unroll
-  for (int mb = 0; mb < D / 32; ++mb)
+    for (int mb = 0; mb < D / 32; ++mb)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      f32x4 a, b;
+      for (int j = 0; j < 4; ++j) {
+        f32x4 a, b;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        a[r] = dka[mb][4 * j + r] * scale;
-        b[r] = dva[mb][4 * j + r];
+        for (int r = 0; r < 4; ++r) {
+          a[r] = dka[mb][4 * j + r] * scale;
+          b[r] = dva[mb][4 * j + r];
+        }
+        const int64_t o = off + (int64_t)key * D + mb * 32 + 8 * j + 4 * h;
+        *reinterpret_cast<f32x4*>(dK + o) = a;
+        *reinterpret_cast<f32x4*>(dV + o) = b;
       }
-      const int64_t o = off + (int64_t)key * D + mb * 32 + 8 * j + 4 * h;
-      *reinterpret_cast<f32x4*>(dK + o) = a;
-      *reinterpret_cast<f32x4*>(dV + o) = b;
-    }
+  }
+  }  // run
 }
 
 // Query-block pass: each wave keeps 32 queries (Q and dO rows as B operands,
@@ -523,19 +627,35 @@ struct BwdQCfg {
   static constexpr int kTile = kKT * D;
 };
 
+// dS^T of a 32-key x 32-query slice in B-operand chunks (query column per
+// lane); lse2 = lse * log2(e) and dl = rowsum(dO*O) of the lane's query.
+template <bool kMask>
+__device__ __forceinline__ void q_weights(const f32x16& sacc, const f32x16& dpacc, float lse2,
+                                          float dl, float sl2, int kbase, int h, int query,
+                                          bf16x8 (&dsch)[2]) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    float p = fexp2(__builtin_fmaf(sacc[i], sl2, -lse2));
+    if (kMask && kbase + 8 * (i >> 2) + 4 * h + (i & 3) > query) p = 0.f;
+    dsch[i >> 3][i & 7] = static_cast<__bf16>(p * (dpacc[i] - dl));
+  }
+}
+
 template <int D, int WAVES, int MINW>
 __global__ __launch_bounds__(64 * WAVES, MINW) void attn_bwd_dq_bf16(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
-    const __bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ DELTA,
-    float* __restrict__ dQ, int S, float sl2, float scale) {
+    const __bf16* __restrict__ dO, const float* __restrict__ LSE2, const float* __restrict__ DELTA,
+    float* __restrict__ dQ, int S, float sl2, float scale, int paired) {
   using C = BwdQCfg<D, WAVES>;
   __shared__ __attribute__((aligned(1024))) __bf16 sKV[2][2][C::kTile];  // [buffer][K, V]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, c32 = lane & 31;
   const int nqb = (S + C::kQB - 1) / C::kQB;
-  int head, qblk;
-  map_block(blockIdx.x, gridDim.x, gridDim.x / nqb, nqb, head, qblk);
-  const int64_t bh = head;
+  const Runs runs = plan_runs(blockIdx.x, gridDim.x, nqb, paired);
+  const int64_t bh = runs.head;
+  for (int run = 0; run < runs.n; ++run) {
+  if (run > 0) __syncthreads();  // every wave is done with the LDS tiles
+  const int qblk = nqb - 1 - runs.rank[run];
   const int q0 = qblk * C::kQB;
   const int qw0 = q0 + wave * C::kQW;
   const int query = qw0 + c32;
@@ -552,7 +672,7 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void attn_bwd_dq_bf16(
     qreg[dc] = query < S ? *reinterpret_cast<const bf16x8*>(Q + off + (int64_t)query * D + dc * 16 + 8 * h) : zero8();
     doreg[dc] = query < S ? *reinterpret_cast<const bf16x8*>(dO + off + (int64_t)query * D + dc * 16 + 8 * h) : zero8();
   }
-  const float lse2 = query < S ? LSE[bh * (int64_t)S + query] * kLog2e : 0.f;
+  const float lse2 = query < S ? LSE2[bh * (int64_t)S + query] : 0.f;
   const float dl = query < S ? DELTA[bh * (int64_t)S + query] : 0.f;
   f32x16 dqa[D / 32];
 #pragma unroll
@@ -579,15 +699,11 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void attn_bwd_dq_bf16(
         sacc = mfma32(rd_rows<D>(sK, kb * 32 + c32, 2 * dc + h), qreg[dc], sacc);
         dpacc = mfma32(rd_rows<D>(sV, kb * 32 + c32, 2 * dc + h), doreg[dc], dpacc);
       }
-      const bool diag = kbase + 31 > qw0;
       bf16x8 dsch[2];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int kk = kbase + 8 * (i >> 2) + 4 * h + (i & 3);
-        float p = fexp2(__builtin_fmaf(sacc[i], sl2, -lse2));
-        if (diag && kk > query) p = 0.f;
-        dsch[i >> 3][i & 7] = static_cast<__bf16>(p * (dpacc[i] - dl));
-      }
+      if (kbase + 31 > qw0)  // diagonal slice (wave-uniform)
+        q_weights<true>(sacc, dpacc, lse2, dl, sl2, kbase, h, query, dsch);
+      else
+        q_weights<false>(sacc, dpacc, lse2, dl, sl2, kbase, h, query, dsch);
 #pragma unroll
       for (int c = 0; c < 2; ++c)
 #pragma unroll
@@ -595,16 +711,18 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void attn_bwd_dq_bf16(
           dqa[mb] = mfma32(rd_tr8<D>(sK, kb * 32 + 16 * c + 4 * h, mb * 32, lane), dsch[c], dqa[mb]);
     }
   }
-  if (query >= S) return;
+  if (query < S) {
 #pragma unroll
-  for (int mb = 0; mb < D / 32; ++mb)
+    for (int mb = 0; mb < D / 32; ++mb)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      f32x4 a;
+      for (int j = 0; j < 4; ++j) {
+        f32x4 a;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) a[r] = dqa[mb][4 * j + r] * scale;
-      *reinterpret_cast<f32x4*>(dQ + off + (int64_t)query * D + mb * 32 + 8 * j + 4 * h) = a;
-    }
+        for (int r = 0; r < 4; ++r) a[r] = dqa[mb][4 * j + r] * scale;
+        *reinterpret_cast<f32x4*>(dQ + off + (int64_t)query * D + mb * 32 + 8 * j + 4 * h) = a;
+      }
+  }
+  }  // run
 }
 
 }  // namespace
@@ -629,29 +747,37 @@ hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, float* o
   const auto V = static_cast<const __bf16*>(v);
   if (d == 64) {
     using C = FwdCfg<64, LH_FWD64_QW, LH_FWD64_WAVES>;
-    const dim3 grid((unsigned)((S + C::kQB - 1) / C::kQB * BH));
-    attn_fwd_bf16<64, LH_FWD64_QW, LH_FWD64_WAVES, LH_FWD64_MINW><<<grid, C::kThreads, 0, st>>>(
-        Q, K, V, o, lse, (int)S, sl2);
+    const int64_t nb = (S + C::kQB - 1) / C::kQB;
+    const bool pr = LH_PAIR_FWD && pair_blocks(nb, BH);
+    attn_fwd_bf16<64, LH_FWD64_QW, LH_FWD64_WAVES, LH_FWD64_MINW>
+        <<<dim3((unsigned)causal_grid(nb, BH, pr)), C::kThreads, 0, st>>>(Q, K, V, o, lse, (int)S,
+                                                                          sl2, pr ? 1 : 0);
   } else {
     using C = FwdCfg<128, LH_FWD128_QW, LH_FWD128_WAVES>;
-    const dim3 grid((unsigned)((S + C::kQB - 1) / C::kQB * BH));
-    attn_fwd_bf16<128, LH_FWD128_QW, LH_FWD128_WAVES, LH_FWD128_MINW><<<grid, C::kThreads, 0, st>>>(
-        Q, K, V, o, lse, (int)S, sl2);
+    const int64_t nb = (S + C::kQB - 1) / C::kQB;
+    const bool pr = LH_PAIR_FWD && pair_blocks(nb, BH);
+    attn_fwd_bf16<128, LH_FWD128_QW, LH_FWD128_WAVES, LH_FWD128_MINW>
+        <<<dim3((unsigned)causal_grid(nb, BH, pr)), C::kThreads, 0, st>>>(Q, K, V, o, lse, (int)S,
+                                                                          sl2, pr ? 1 : 0);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_attn_bwd(const void* q, const void* k, const void* v, const float* o,
                            const float* lse, const void* dout, float* dq, float* dk, float* dv,
-                           float* delta, int64_t S, int d, int dtype, int64_t BH,
+                           float* delta, float* lse2, int64_t S, int d, int dtype, int64_t BH,
                            hipStream_t st, hipEvent_t* ev) {
   if (S == 0) return hipSuccess;
   const int64_t rows = S * BH;
   const int rgs = 256 / (d / 8);
   const unsigned dgrid = (unsigned)((rows + rgs - 1) / rgs);
   const bool f32 = dtype == 0;
-  if (f32) attn_delta<float><<<dgrid, 256, 0, st>>>(o, static_cast<const float*>(dout), delta, rows, d);
-  else attn_delta<__bf16><<<dgrid, 256, 0, st>>>(o, static_cast<const __bf16*>(dout), delta, rows, d);
+  if (f32)
+    attn_delta<float><<<dgrid, 256, 0, st>>>(o, static_cast<const float*>(dout), lse, delta,
+                                             nullptr, rows, d);
+  else
+    attn_delta<__bf16><<<dgrid, 256, 0, st>>>(o, static_cast<const __bf16*>(dout), lse, delta,
+                                              lse2, rows, d);
   hipError_t e = hipGetLastError();
   if (e == hipSuccess && ev) e = hipEventRecord(ev[0], st);
   if (e != hipSuccess) return e;
@@ -669,28 +795,36 @@ hipError_t launch_attn_bwd(const void* q, const void* k, const void* v, const fl
   const auto G = static_cast<const __bf16*>(dout);
   if (d == 64) {
     using C1 = BwdKVCfg<64, LH_BKV64_WAVES>;
-    const dim3 g1((unsigned)((S + C1::kKB - 1) / C1::kKB * BH));
-    attn_bwd_dkdv_bf16<64, LH_BKV64_WAVES, LH_BKV64_MINW><<<g1, 64 * LH_BKV64_WAVES, 0, st>>>(
-        Q, K, V, G, lse, delta, dk, dv, (int)S, sl2, scale);
+    const int64_t nb = (S + C1::kKB - 1) / C1::kKB;
+    const bool pr = LH_PAIR_BKV64 && pair_blocks(nb, BH);
+    attn_bwd_dkdv_bf16<64, LH_BKV64_WAVES, LH_BKV64_MINW>
+        <<<dim3((unsigned)causal_grid(nb, BH, pr)), 64 * LH_BKV64_WAVES, 0, st>>>(
+            Q, K, V, G, lse2, delta, dk, dv, (int)S, sl2, scale, pr ? 1 : 0);
   } else {
     using C1 = BwdKVCfg<128, LH_BKV128_WAVES>;
-    const dim3 g1((unsigned)((S + C1::kKB - 1) / C1::kKB * BH));
-    attn_bwd_dkdv_bf16<128, LH_BKV128_WAVES, LH_BKV128_MINW><<<g1, 64 * LH_BKV128_WAVES, 0, st>>>(
-        Q, K, V, G, lse, delta, dk, dv, (int)S, sl2, scale);
+    const int64_t nb = (S + C1::kKB - 1) / C1::kKB;
+    const bool pr = LH_PAIR_BKV128 && pair_blocks(nb, BH);
+    attn_bwd_dkdv_bf16<128, LH_BKV128_WAVES, LH_BKV128_MINW>
+        <<<dim3((unsigned)causal_grid(nb, BH, pr)), 64 * LH_BKV128_WAVES, 0, st>>>(
+            Q, K, V, G, lse2, delta, dk, dv, (int)S, sl2, scale, pr ? 1 : 0);
   }
   e = hipGetLastError();
   if (e == hipSuccess && ev) e = hipEventRecord(ev[1], st);
   if (e != hipSuccess) return e;
   if (d == 64) {
     using C2 = BwdQCfg<64, LH_BQ64_WAVES>;
-    const dim3 g2((unsigned)((S + C2::kQB - 1) / C2::kQB * BH));
-    attn_bwd_dq_bf16<64, LH_BQ64_WAVES, LH_BQ64_MINW><<<g2, 64 * LH_BQ64_WAVES, 0, st>>>(
-        Q, K, V, G, lse, delta, dq, (int)S, sl2, scale);
+    const int64_t nb = (S + C2::kQB - 1) / C2::kQB;
+    const bool pr = LH_PAIR_BQ && pair_blocks(nb, BH);
+    attn_bwd_dq_bf16<64, LH_BQ64_WAVES, LH_BQ64_MINW>
+        <<<dim3((unsigned)causal_grid(nb, BH, pr)), 64 * LH_BQ64_WAVES, 0, st>>>(
+            Q, K, V, G, lse2, delta, dq, (int)S, sl2, scale, pr ? 1 : 0);
   } else {
     using C2 = BwdQCfg<128, LH_BQ128_WAVES>;
-    const dim3 g2((unsigned)((S + C2::kQB - 1) / C2::kQB * BH));
-    attn_bwd_dq_bf16<128, LH_BQ128_WAVES, LH_BQ128_MINW><<<g2, 64 * LH_BQ128_WAVES, 0, st>>>(
-        Q, K, V, G, lse, delta, dq, (int)S, sl2, scale);
+    const int64_t nb = (S + C2::kQB - 1) / C2::kQB;
+    const bool pr = LH_PAIR_BQ && pair_blocks(nb, BH);
+    attn_bwd_dq_bf16<128, LH_BQ128_WAVES, LH_BQ128_MINW>
+        <<<dim3((unsigned)causal_grid(nb, BH, pr)), 64 * LH_BQ128_WAVES, 0, st>>>(
+            Q, K, V, G, lse2, delta, dq, (int)S, sl2, scale, pr ? 1 : 0);
   }
   e = hipGetLastError();
   if (e == hipSuccess && ev) e = hipEventRecord(ev[2], st);

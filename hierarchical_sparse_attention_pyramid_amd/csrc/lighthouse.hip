@@ -152,10 +152,10 @@ lh_status make_plan(const lh_shape* s, Plan& P) {
   z.ws_score = 0;
   z.ws_topk = z.K > 0 ? align_up(lh::topk_ws_bytes(BH, z.C)) : 0;
   z.ws_gather = 0;
-  z.ws_attention_backward = align_up(z.bytes_lse);
+  z.ws_attention_backward = 2 * align_up(z.bytes_lse);  // rowsum(dO*O), lse*log2(e)
   z.ws_scatter_backward = sums1;
   z.ws_forward = std::max(z.ws_build_pyramid, z.ws_topk);
-  z.ws_backward = align_up(z.bytes_sub) + 3 * align_up(z.bytes_sub_f32) + align_up(z.bytes_lse) +
+  z.ws_backward = align_up(z.bytes_sub) + 3 * align_up(z.bytes_sub_f32) + z.ws_attention_backward +
                   z.ws_scatter_backward;
   return LH_OK;
 }
@@ -453,9 +453,10 @@ lh_status lh_attention_backward(const lh_shape* shape, const void* qs, const voi
   LH_NEED(dks, "dks");
   LH_NEED(dvs, "dvs");
   if ((s = check_ws(ws, ws_bytes, P.sz.ws_attention_backward)) != LH_OK) return s;
-  LH_HIP(lh::launch_attn_bwd(qs, ks, vs, os, lse, dos, dqs, dks, dvs, static_cast<float*>(ws),
-                             P.g.S, P.g.d, P.dtype, P.BH, static_cast<hipStream_t>(stream),
-                             nullptr),
+  float* delta = static_cast<float*>(ws);
+  float* lse2 = reinterpret_cast<float*>(static_cast<char*>(ws) + align_up(P.sz.bytes_lse));
+  LH_HIP(lh::launch_attn_bwd(qs, ks, vs, os, lse, dos, dqs, dks, dvs, delta, lse2, P.g.S, P.g.d,
+                             P.dtype, P.BH, static_cast<hipStream_t>(stream), nullptr),
          "attention_backward");
   return LH_OK;
 }
@@ -518,12 +519,13 @@ static lh_status run_backward(const Plan& P, const void* dout, const lh_buffers*
   float* dvs = reinterpret_cast<float*>(w);
   w += align_up(P.sz.bytes_sub_f32);
   float* delta = reinterpret_cast<float*>(w);
-  w += align_up(P.sz.bytes_lse);
+  float* lse2 = reinterpret_cast<float*>(w + align_up(P.sz.bytes_lse));
+  w += P.sz.ws_attention_backward;
   lh_status s;
   if ((s = run_scatter_bwd(P, dout, b->pos, dos, w, st)) != LH_OK) return s;
   if (ev) LH_HIP(hipEventRecord(ev[0], st), "event");
-  LH_HIP(lh::launch_attn_bwd(b->qs, b->ks, b->vs, b->os, b->lse, dos, dqs, dks, dvs, delta, P.g.S,
-                             P.g.d, P.dtype, P.BH, st, ev ? ev + 1 : nullptr),
+  LH_HIP(lh::launch_attn_bwd(b->qs, b->ks, b->vs, b->os, b->lse, dos, dqs, dks, dvs, delta, lse2,
+                             P.g.S, P.g.d, P.dtype, P.BH, st, ev ? ev + 1 : nullptr),
          "attention_backward");
   lh::BcastArgs a{};
   a.src[0] = dqs;
