@@ -28,37 +28,54 @@ __device__ __forceinline__ int32_t div_pw(int32_t t, const Geo& g, int l) {
   return g.log2p >= 0 ? (t >> (g.log2p * l)) : t / g.pw[l];
 }
 
+// Vector loads and stores; the streaming forms (NT = true) mark data that is
+// touched once, so that it does not displace reused lines in the caches.
+template <bool NT, typename V>
+__device__ __forceinline__ V ld(const V* p) {
+  if constexpr (NT) return __builtin_nontemporal_load(p);
+  else return *p;
+}
+template <bool NT, typename V>
+__device__ __forceinline__ void st(V* p, const V& v) {
+  if constexpr (NT) __builtin_nontemporal_store(v, p);
+  else *p = v;
+}
+
 // ---- 8-element row slices (16 bytes of bf16, 32 bytes of fp32) ----------
 template <typename T> struct Row8;
 
 template <> struct Row8<float> {
+  template <bool NT = false>
   static __device__ __forceinline__ void load(const float* p, float (&x)[8]) {
-    const f32x4 a = reinterpret_cast<const f32x4*>(p)[0];
-    const f32x4 b = reinterpret_cast<const f32x4*>(p)[1];
+    const f32x4 a = ld<NT>(reinterpret_cast<const f32x4*>(p));
+    const f32x4 b = ld<NT>(reinterpret_cast<const f32x4*>(p) + 1);
 #pragma unroll
     for (int e = 0; e < 4; ++e) { x[e] = a[e]; x[e + 4] = b[e]; }
   }
+  template <bool NT = false>
   static __device__ __forceinline__ void store(float* p, const float (&x)[8]) {
     f32x4 a, b;
 #pragma unroll
     for (int e = 0; e < 4; ++e) { a[e] = x[e]; b[e] = x[e + 4]; }
-    reinterpret_cast<f32x4*>(p)[0] = a;
-    reinterpret_cast<f32x4*>(p)[1] = b;
+    st<NT>(reinterpret_cast<f32x4*>(p), a);
+    st<NT>(reinterpret_cast<f32x4*>(p) + 1, b);
   }
 };
 
 template <> struct Row8<__bf16> {
+  template <bool NT = false>
   static __device__ __forceinline__ void load(const __bf16* p, float (&x)[8]) {
-    const bf16x8 v = *reinterpret_cast<const bf16x8*>(p);
+    const bf16x8 v = ld<NT>(reinterpret_cast<const bf16x8*>(p));
 #pragma unroll
     for (int e = 0; e < 8; ++e) x[e] = static_cast<float>(v[e]);
   }
   // float -> bf16 rounds to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+  template <bool NT = false>
   static __device__ __forceinline__ void store(__bf16* p, const float (&x)[8]) {
     bf16x8 v;
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[e] = static_cast<__bf16>(x[e]);
-    *reinterpret_cast<bf16x8*>(p) = v;
+    st<NT>(reinterpret_cast<bf16x8*>(p), v);
   }
 };
 

@@ -21,7 +21,17 @@ namespace lh {
 
 namespace {
 
-constexpr int kRowsInFlight = 4;  // rows whose loads a row group issues together
+#ifndef LH_POOL_ROWS
+#define LH_POOL_ROWS 4
+#endif
+#ifndef LH_POOL_NT
+#define LH_POOL_NT 1
+#endif
+#ifndef LH_POOL_QKV1
+#define LH_POOL_QKV1 0
+#endif
+constexpr int kRowsInFlight = LH_POOL_ROWS;  // rows whose loads a row group issues together
+constexpr bool kStream = LH_POOL_NT != 0;    // token rows are read once: streaming loads
 
 // ||x||_2 of a d-long row spread over `lpr` lanes (element 8*lane + e in
 // x[e]), in the fixed float32 order: squares, then the halving tree
@@ -86,7 +96,7 @@ __device__ __forceinline__ void pool_pass(const PoolFwdArgs& a, const int (&tid)
       for (int u = 0; u < kRowsInFlight; ++u) {
         const int64_t row = r0 + min(rb + u, nrows - 1);
 #pragma unroll
-        for (int i = 0; i < NT; ++i) Row8<Tin>::load(in[i] + row * d, xs[u][i]);
+        for (int i = 0; i < NT; ++i) Row8<Tin>::template load<kStream>(in[i] + row * d, xs[u][i]);
       }
     }
     float sin[kRowsInFlight];
@@ -126,7 +136,7 @@ __device__ __forceinline__ void pool_pass(const PoolFwdArgs& a, const int (&tid)
             float m[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) m[e] = acc[l][i][e] * g.inv_pw[lev];
-            Row8<Tout>::store(pyr[i] + (int64_t)(g.base[lev] - g.N + j) * d, m);
+            Row8<Tout>::template store<kStream>(pyr[i] + (int64_t)(g.base[lev] - g.N + j) * d, m);
           }
         }
         if constexpr (SCORE != 0) {
@@ -169,6 +179,12 @@ __global__ __launch_bounds__(256) void pool_fwd_kernel(PoolFwdArgs a, int do_poo
   constexpr int kScore = FIRST ? 1 : 2;
   // pass 1: q and k (with the scores); pass 2: v
   const int qk[2] = {0, 1};
+  if (LH_POOL_QKV1 && do_pool) {
+    const int qkv[3] = {0, 1, 2};
+    if (do_score) pool_pass<Tin, Tout, 3, kScore>(a, qkv, true, bh, r0, nrows, lane);
+    else pool_pass<Tin, Tout, 3, 0>(a, qkv, true, bh, r0, nrows, lane);
+    return;
+  }
   if (do_score) {
     pool_pass<Tin, Tout, 2, kScore>(a, qk, do_pool != 0, bh, r0, nrows, lane);
   } else if (do_pool) {
@@ -217,7 +233,7 @@ __global__ __launch_bounds__(256) void pool_bwd_kernel(PoolBwdArgs a) {
 #pragma unroll
     for (int u = 0; u < kRowsInFlight; ++u) {
       const int64_t row = r0 + min(rb + u, nrows - 1);
-      Row8<Tin>::load(in + row * d, xs[u]);
+      Row8<Tin>::template load<kStream>(in + row * d, xs[u]);
       if constexpr (FIRST) pt[u] = pos[row];
     }
 #pragma unroll

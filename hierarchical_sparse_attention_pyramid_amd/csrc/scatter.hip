@@ -23,9 +23,19 @@ namespace lh {
 
 namespace {
 
-constexpr int kE = 4;              // elements per lane (16-byte float32 source loads)
-constexpr int kTokPerGroup = 64;   // consecutive tokens walked by one row group
-constexpr int kU = 4;              // tokens whose level-0 loads are issued together
+#ifndef LH_BC_TOK
+#define LH_BC_TOK 64
+#endif
+#ifndef LH_BC_U
+#define LH_BC_U 4
+#endif
+#ifndef LH_BC_NTS
+#define LH_BC_NTS 1
+#endif
+constexpr int kE = 4;                    // elements per lane (16-byte float32 source loads)
+constexpr int kTokPerGroup = LH_BC_TOK;  // consecutive tokens walked by one row group
+constexpr int kU = LH_BC_U;              // tokens whose level-0 loads are issued together
+constexpr bool kStreamOut = LH_BC_NTS != 0;  // outputs are written once: streaming stores
 
 template <typename Tout> struct Out4;
 template <> struct Out4<float> {
@@ -33,7 +43,7 @@ template <> struct Out4<float> {
     f32x4 v;
 #pragma unroll
     for (int e = 0; e < kE; ++e) v[e] = x[e];
-    *reinterpret_cast<f32x4*>(p) = v;
+    st<kStreamOut>(reinterpret_cast<f32x4*>(p), v);
   }
 };
 template <> struct Out4<__bf16> {
@@ -41,7 +51,7 @@ template <> struct Out4<__bf16> {
     bf16x4 v;
 #pragma unroll
     for (int e = 0; e < kE; ++e) v[e] = static_cast<__bf16>(x[e]);
-    *reinterpret_cast<bf16x4*>(p) = v;
+    st<kStreamOut>(reinterpret_cast<bf16x4*>(p), v);
   }
 };
 
