@@ -124,62 +124,112 @@ typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 
 template <int D>
-__device__ __forceinline__ int swz(int r) {
+__host__ __device__ constexpr int swz(int r) {
   if constexpr (D == 64) return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
   else return ((r & 3) << 2) | ((r >> 2) & 3);
 }
 
 // byte offset of logical 16-byte chunk x of row r in a swizzled tile
 template <int D>
-__device__ __forceinline__ int toff(int r, int x) {
+__host__ __device__ constexpr int toff(int r, int x) {
   return r * (D * 2) + ((x ^ swz<D>(r)) << 4);
 }
 
+// swz is a permutation of the low row bits, so toff is linear over XOR:
+// toff(rc ^ rl, xc ^ xl) = toff(rc, xc) ^ toff(rl, xl) whenever rc and rl
+// (and xc and xl) occupy disjoint bits, and rows that are multiples of 16
+// have swz = 0, so they only add r * 2D.  Every read address below is
+// (lane part ^ chunk part) + row part: the lane part (with the tile's byte
+// offset, a multiple of the tile size) is formed once per tile, the few
+// distinct chunk parts cost one XOR each per tile, and the row part is an
+// immediate offset of the LDS instruction.  Where registers are scarcest,
+// kEach = true folds every part into one XOR per read instead, so that no
+// per-tile chunk parts stay live.
+
+// Buffer descriptor (raw, stride 0) of `bytes` bytes from p: loads at
+// offsets >= bytes return zero.
+constexpr int kBufWord3 = 0x00020000;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, bytes, kBufWord3);
+}
+
 // Asynchronously copy rows [r0, r0 + R) of a [S][D] bf16 tensor into a
-// swizzled LDS tile; rows >= S repeat row S-1 (they are masked or unused).
-// Waves w = wave, wave + NW, ... of the workgroup split the instructions.
+// swizzled LDS tile with direct buffer loads (16 bytes per lane; lane l of
+// one instruction lands at byte 16*l of a 1 KB run).  The descriptor covers
+// rows [r0, S), so rows >= S read as zero (they are masked or unused), and
+// each instruction needs only a 32-bit lane offset.  Waves w = wave,
+// wave + NW, ... of the workgroup split the instructions.
 template <int D, int R, int NW>
 __device__ __forceinline__ void load_tile(const __bf16* src, int S, int r0, __bf16* tile, int wave,
                                           int lane) {
   constexpr int kCPR = D / 8;
   constexpr int kInst = R * kCPR / 64;
+  const int rows = S > r0 ? S - r0 : 0;
+  const __amdgpu_buffer_rsrc_t rs = rsrc(src + (int64_t)r0 * D, rows * D * 2);
 #pragma unroll
   for (int n = wave; n < kInst; n += NW) {
     const int p = n * 64 + lane;
     const int r = p / kCPR, pc = p % kCPR;
     const int x = pc ^ swz<D>(r);
-    const int row = min(r0 + r, S - 1);
-    __builtin_amdgcn_global_load_lds(src + (int64_t)row * D + x * 8,
-                                     (lds_void*)(tile + n * 512), 16, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(tile + n * 512), 16,
+                                             (r * D + x * 8) * 2, 0, 0, 0);
   }
 }
 
 __device__ __forceinline__ void wait_loads() { __builtin_amdgcn_s_waitcnt(0); }
 
-// A operand from rows (MFMA row = tile row r, contraction = 8 elements of
-// logical chunk x)
+// Row reads (A operand): lane (h, c) reads tile row rc + c, logical chunk
+// 2*dc + h (rc a multiple of 32).
 template <int D>
-__device__ __forceinline__ bf16x8 rd_rows(const __bf16* tile, int r, int x) {
-  return *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(tile) + toff<D>(r, x));
+__device__ __forceinline__ uint32_t lane_rows(int lane) {
+  return (uint32_t)(toff<D>(lane & 31, 0) ^ ((lane >> 5) << 4));
 }
 
-// A operand transposed: lane (h, c) of the wave gets column c0 + c%16 + 16*(c/16)
-// ... precisely: lane l (group G = l/16, j = l%16) reads row r0 + j/4 at
-// columns cb + 16*(G&1) + 4*(j%4); the result holds column cb + (l%32) of
-// rows r0..r0+3.  Two such reads (rows r0 and r0 + 8) form one operand.
+__device__ __forceinline__ bf16x8 lds_rows_at(const void* base, uint32_t off) {
+  return *reinterpret_cast<const bf16x8*>(static_cast<const char*>(base) + off);
+}
 template <int D>
-__device__ __forceinline__ bf16x4 rd_tr(const __bf16* tile, int r0, int cb, int lane) {
+constexpr uint32_t cst_rows(int rc, int dc) {
+  return (uint32_t)(rc * D * 2 + (dc << 5));
+}
+template <int D>
+constexpr uint32_t cst_tr(int rc, int cb) {
+  return (uint32_t)toff<D>(rc, cb >> 3);
+}
+
+template <int D, bool kEach = false>
+__device__ __forceinline__ bf16x8 lds_rows(const void* base, uint32_t lane_t, int rc, int dc) {
+  const char* b = static_cast<const char*>(base);
+  if constexpr (kEach)
+    return lds_rows_at(base, lane_t ^ cst_rows<D>(rc, dc));
+  else
+    return *reinterpret_cast<const bf16x8*>(b + (lane_t ^ (uint32_t)(dc << 5)) + rc * D * 2);
+}
+
+// Transposed reads (A operand from a row-major tile): lane l (group G = l/16,
+// j = l%16, h = l/32) reads row rc + 4h + j/4 at columns cb + 16*(G&1) +
+// 4*(j%4) .. +3; the result holds column cb + (l%32) of rows rc + 4h .. +3.
+// Reads at rows rc and rc + 8 form one operand (rc a multiple of 16, cb of
+// 32).
+template <int D>
+__device__ __forceinline__ uint32_t lane_tr(int lane) {
   const int j = lane & 15, G = lane >> 4;
-  const int r = r0 + (j >> 2);
-  const int col = cb + 16 * (G & 1) + 4 * (j & 3);
-  const char* p = reinterpret_cast<const char*>(tile) + toff<D>(r, col >> 3) + ((col & 7) << 1);
-  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p);
+  const int rl = 4 * (G >> 1) + (j >> 2);
+  const int xl = 2 * (G & 1) + ((j & 3) >> 1);
+  return (uint32_t)(toff<D>(rl, xl) + 8 * (j & 1));
 }
-
-template <int D>
-__device__ __forceinline__ bf16x8 rd_tr8(const __bf16* tile, int r0, int cb, int lane) {
-  const bf16x4 lo = rd_tr<D>(tile, r0, cb, lane);
-  const bf16x4 hi = rd_tr<D>(tile, r0 + 8, cb, lane);
+template <int D, bool kEach = false>
+__device__ __forceinline__ bf16x8 lds_tr8(const void* base, uint32_t lane_t, int rc, int cb) {
+  const char* b = static_cast<const char*>(base);
+  bf16x4 lo, hi;
+  if constexpr (kEach) {
+    lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(b + (lane_t ^ cst_tr<D>(rc, cb))));
+    hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(b + (lane_t ^ cst_tr<D>(rc + 8, cb))));
+  } else {
+    const char* br = b + rc * D * 2;
+    lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(br + (lane_t ^ (uint32_t)toff<D>(0, cb >> 3))));
+    hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(br + (lane_t ^ (uint32_t)toff<D>(8, cb >> 3))));
+  }
   bf16x8 a;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
@@ -285,14 +335,16 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void attn_fwd_bf16(
   using C = FwdCfg<D, QW, WAVES>;
   constexpr int NQB = C::kNQB;
   __shared__ __attribute__((aligned(1024))) __bf16 sKV[2][2][C::kTile];  // [buffer][K,V]
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
   const int h = lane >> 5, c32 = lane & 31;
+  const uint32_t lrow = lane_rows<D>(lane), ltr = lane_tr<D>(lane);
   const int nqb = (S + C::kQB - 1) / C::kQB;
   const Runs runs = plan_runs(blockIdx.x, gridDim.x, nqb, paired);
-  const int64_t bh = runs.head;
+  const int64_t bh = __builtin_amdgcn_readfirstlane(runs.head);
   for (int run = 0; run < runs.n; ++run) {
   if (run > 0) __syncthreads();  // every wave is done with the LDS tiles
-  const int qblk = nqb - 1 - runs.rank[run];
+  const int qblk = nqb - 1 - __builtin_amdgcn_readfirstlane(runs.rank[run]);
   const int q0 = qblk * C::kQB;
   const int qw0 = q0 + wave * C::kQW;
   const __bf16* Qh = Q + bh * (int64_t)S * D;
@@ -334,8 +386,10 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void attn_fwd_bf16(
       load_tile<D, C::kKT, WAVES>(Vh, S, k0 + C::kKT, sKV[(kt + 1) & 1][1], wave, lane);
     }
     if (qw0 >= S || k0 > qw0 + C::kQW - 1) continue;  // nothing visible for this wave
-    const __bf16* sK = sKV[kt & 1][0];
-    const __bf16* sV = sKV[kt & 1][1];
+    // lane parts of this tile's reads (K and V tiles of buffer kt & 1)
+    const uint32_t kbo = (uint32_t)((kt & 1) * 2 * C::kTile * 2);
+    const uint32_t lk = lrow ^ kbo;
+    const uint32_t lv = ltr ^ (kbo + C::kTile * 2);
 
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
@@ -348,7 +402,7 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void attn_fwd_bf16(
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int dc = 0; dc < D / 16; ++dc) kop[kb][dc] = rd_rows<D>(sK, kb * 32 + c32, 2 * dc + h);
+        for (int dc = 0; dc < D / 16; ++dc) kop[kb][dc] = lds_rows<D>(sKV, lk, kb * 32, dc);
       bf16x8 vop[2][2][D / 32];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -356,7 +410,7 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void attn_fwd_bf16(
         for (int c = 0; c < 2; ++c)
 #pragma unroll
           for (int mb = 0; mb < D / 32; ++mb)
-            vop[kb][c][mb] = rd_tr8<D>(sV, kb * 32 + 16 * c + 4 * h, mb * 32, lane);
+            vop[kb][c][mb] = lds_tr8<D>(sKV, lv, kb * 32 + 16 * c, mb * 32);
       f32x16 sacc[2] = {zero16(), zero16()};
 #pragma unroll
       for (int dc = 0; dc < D / 16; ++dc)
@@ -467,9 +521,11 @@ __global__ __launch_bounds__(256) void attn_delta(const float* __restrict__ O, c
 }
 
 // Stage 64 float32 values (lse or delta of a query tile) into LDS with one
-// direct load (4 bytes per lane); rows >= S repeat row S-1.
+// direct load (4 bytes per lane); rows >= S read as zero (masked queries).
 __device__ __forceinline__ void load_vec64(const float* src, int S, int r0, float* dst, int lane) {
-  __builtin_amdgcn_global_load_lds(src + min(r0 + lane, S - 1), (lds_void*)dst, 4, 0, 0);
+  const int rows = S > r0 ? S - r0 : 0;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc(src + r0, rows * 4), (lds_void*)dst, 4, lane * 4, 0,
+                                           0, 0);
 }
 
 // Key-block pass: each wave keeps 32 keys (K and V rows as MFMA B operands)
@@ -511,17 +567,21 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void attn_bwd_dkdv_bf16(
   // d = 128: the wave's 32 V rows live in LDS instead of registers (the
   // register file would otherwise spill); they are the B operand of dP.
   constexpr bool kVInLds = D == 128 && LH_BKV128_VLDS;
+  constexpr bool kEach = D == 128;  // register budget: one XOR per LDS read
   __shared__ __attribute__((aligned(1024))) __bf16 sT[2][2][C::kTile];  // [buffer][Q, dO]
   __shared__ __attribute__((aligned(1024))) __bf16 sVw[kVInLds ? WAVES : 1][kVInLds ? 32 * D : 8];
   __shared__ float sLD[2][2][C::kQT];                                  // [buffer][lse, delta]
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
   const int h = lane >> 5, c32 = lane & 31;
+  const uint32_t lrow = lane_rows<D>(lane), ltr = lane_tr<D>(lane);
+  const uint32_t lvw = lrow ^ (uint32_t)(kVInLds ? wave * 32 * D * 2 : 0);  // this wave's V rows
   const int nkb = (S + C::kKB - 1) / C::kKB;
   const Runs runs = plan_runs(blockIdx.x, gridDim.x, nkb, paired);
-  const int64_t bh = runs.head;
+  const int64_t bh = __builtin_amdgcn_readfirstlane(runs.head);
   for (int run = 0; run < runs.n; ++run) {
   if (run > 0) __syncthreads();  // every wave is done with the LDS tiles
-  const int kblk = runs.rank[run];  // early keys (most queries) are the heavy end
+  const int kblk = __builtin_amdgcn_readfirstlane(runs.rank[run]);  // early keys (most queries) are the heavy end
   const int kb0 = kblk * C::kKB;
   const int kw0 = kb0 + wave * C::kKW;
   const int key = kw0 + c32;
@@ -564,20 +624,25 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void attn_bwd_dkdv_bf16(
     __syncthreads();
     if (t + 1 < ntiles) issue(t + 1, buf ^ 1);
     if (kw0 >= S || q0 + C::kQT - 1 < kw0) continue;
-    const __bf16* sQ = sT[buf][0];
-    const __bf16* sG = sT[buf][1];
+    const uint32_t tbo = (uint32_t)(buf * 2 * C::kTile * 2);  // Q tile; the dO tile follows
+    const uint32_t lvt = lvw;
+    const uint32_t lq = lrow ^ tbo, lg = lrow ^ (tbo + C::kTile * 2);
+    const uint32_t tq = ltr ^ tbo, tg = ltr ^ (tbo + C::kTile * 2);
     const float* sL = sLD[buf][0];
     const float* sD = sLD[buf][1];
 #pragma unroll
     for (int qs = 0; qs < 2; ++qs) {
+      // d = 128: keep the scheduler from hoisting the next slice's reads
+      // (their registers would push live values out to scratch)
+      if constexpr (kEach) __builtin_amdgcn_sched_barrier(0);
       const int qbase = q0 + qs * 32;
       if (qbase + 31 < kw0) continue;
       f32x16 sacc = zero16(), dpacc = zero16();
 #pragma unroll
       for (int dc = 0; dc < D / 16; ++dc) {
-        sacc = mfma32(rd_rows<D>(sQ, qs * 32 + c32, 2 * dc + h), kreg[dc], sacc);
-        const bf16x8 vb = kVInLds ? rd_rows<D>(sVw[wave], c32, 2 * dc + h) : vreg[kVInLds ? 0 : dc];
-        dpacc = mfma32(rd_rows<D>(sG, qs * 32 + c32, 2 * dc + h), vb, dpacc);
+        sacc = mfma32(lds_rows<D, kEach>(sT, lq, qs * 32, dc), kreg[dc], sacc);
+        const bf16x8 vb = kVInLds ? lds_rows<D, kEach>(sVw, lvt, 0, dc) : vreg[kVInLds ? 0 : dc];
+        dpacc = mfma32(lds_rows<D, kEach>(sT, lg, qs * 32, dc), vb, dpacc);
       }
       // Only a slice that meets the diagonal or the end of the sequence needs
       // masks (a wave-uniform branch keeps them off every other slice).
@@ -590,9 +655,8 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void attn_bwd_dkdv_bf16(
       for (int c = 0; c < 2; ++c)
 #pragma unroll
         for (int mb = 0; mb < D / 32; ++mb) {
-          const int r0 = qs * 32 + 16 * c + 4 * h;
-          dva[mb] = mfma32(rd_tr8<D>(sG, r0, mb * 32, lane), pch[c], dva[mb]);
-          dka[mb] = mfma32(rd_tr8<D>(sQ, r0, mb * 32, lane), dsch[c], dka[mb]);
+          dva[mb] = mfma32(lds_tr8<D, kEach>(sT, tg, qs * 32 + 16 * c, mb * 32), pch[c], dva[mb]);
+          dka[mb] = mfma32(lds_tr8<D, kEach>(sT, tq, qs * 32 + 16 * c, mb * 32), dsch[c], dka[mb]);
         }
     }
   }
@@ -648,14 +712,16 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void attn_bwd_dq_bf16(
     float* __restrict__ dQ, int S, float sl2, float scale, int paired) {
   using C = BwdQCfg<D, WAVES>;
   __shared__ __attribute__((aligned(1024))) __bf16 sKV[2][2][C::kTile];  // [buffer][K, V]
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
   const int h = lane >> 5, c32 = lane & 31;
+  const uint32_t lrow = lane_rows<D>(lane), ltr = lane_tr<D>(lane);
   const int nqb = (S + C::kQB - 1) / C::kQB;
   const Runs runs = plan_runs(blockIdx.x, gridDim.x, nqb, paired);
-  const int64_t bh = runs.head;
+  const int64_t bh = __builtin_amdgcn_readfirstlane(runs.head);
   for (int run = 0; run < runs.n; ++run) {
   if (run > 0) __syncthreads();  // every wave is done with the LDS tiles
-  const int qblk = nqb - 1 - runs.rank[run];
+  const int qblk = nqb - 1 - __builtin_amdgcn_readfirstlane(runs.rank[run]);
   const int q0 = qblk * C::kQB;
   const int qw0 = q0 + wave * C::kQW;
   const int query = qw0 + c32;
@@ -687,8 +753,8 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void attn_bwd_dq_bf16(
       load_tile<D, C::kKT, WAVES>(V + off, S, k0 + C::kKT, sKV[(kt + 1) & 1][1], wave, lane);
     }
     if (qw0 >= S || k0 > qw0 + C::kQW - 1) continue;
-    const __bf16* sK = sKV[kt & 1][0];
-    const __bf16* sV = sKV[kt & 1][1];
+    const uint32_t kbo = (uint32_t)((kt & 1) * 2 * C::kTile * 2);  // K tile; the V tile follows
+    const uint32_t lk = lrow ^ kbo, lv = lrow ^ (kbo + C::kTile * 2), tk = ltr ^ kbo;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const int kbase = k0 + kb * 32;
@@ -696,8 +762,8 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void attn_bwd_dq_bf16(
       f32x16 sacc = zero16(), dpacc = zero16();
 #pragma unroll
       for (int dc = 0; dc < D / 16; ++dc) {
-        sacc = mfma32(rd_rows<D>(sK, kb * 32 + c32, 2 * dc + h), qreg[dc], sacc);
-        dpacc = mfma32(rd_rows<D>(sV, kb * 32 + c32, 2 * dc + h), doreg[dc], dpacc);
+        sacc = mfma32(lds_rows<D>(sKV, lk, kb * 32, dc), qreg[dc], sacc);
+        dpacc = mfma32(lds_rows<D>(sKV, lv, kb * 32, dc), doreg[dc], dpacc);
       }
       bf16x8 dsch[2];
       if (kbase + 31 > qw0)  // diagonal slice (wave-uniform)
@@ -708,7 +774,7 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void attn_bwd_dq_bf16(
       for (int c = 0; c < 2; ++c)
 #pragma unroll
         for (int mb = 0; mb < D / 32; ++mb)
-          dqa[mb] = mfma32(rd_tr8<D>(sK, kb * 32 + 16 * c + 4 * h, mb * 32, lane), dsch[c], dqa[mb]);
+          dqa[mb] = mfma32(lds_tr8<D>(sKV, tk, kb * 32 + 16 * c, mb * 32), dsch[c], dqa[mb]);
     }
   }
   if (query < S) {
