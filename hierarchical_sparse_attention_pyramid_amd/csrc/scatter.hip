@@ -32,6 +32,9 @@ namespace {
 #ifndef LH_BC_NTS
 #define LH_BC_NTS 1
 #endif
+#ifndef LH_BC_FAST
+#define LH_BC_FAST 1
+#endif
 constexpr int kE = 4;                    // elements per lane (16-byte float32 source loads)
 constexpr int kTokPerGroup = LH_BC_TOK;  // consecutive tokens walked by one row group
 constexpr int kU = LH_BC_U;              // tokens whose level-0 loads are issued together
@@ -106,10 +109,209 @@ __global__ __launch_bounds__(256) void bcast_kernel(BcastArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Fast path for p a power of two >= 4.  The walk above loads, at every level
+// boundary, an ancestor's position and then (dependent) its row, level by
+// level; here every load of a row group is issued ahead of its use:
+//   * the workgroup first stages in LDS the positions of its tokens and of
+//     all their ancestors (one coalesced burst);
+//   * a row group covers 64 tokens (64 divides every p^l >= 64), so the
+//     "outer" levels with p^l >= 64 contribute the same rows to all of its
+//     tokens: they are summed once, their loads issued together;
+//   * the (at most two) inner levels change at chunk starts only (chunks of
+//     4 tokens, p >= 4); the rows of chunk c+1 (level 0 and the inner levels
+//     that change there) are loaded before chunk c is stored, from two
+//     alternating register buffers.
+// One tensor per row group (gridDim.z = number of tensors).
+constexpr int kFastTok = 64;
+constexpr int kFastU = 4;
+constexpr int kFastInner = 2;      // inner levels handled (p = 4: levels 1, 2)
+constexpr int kFastOuter = 8;      // outer levels summed with loads in flight together
+constexpr int kPosCache = 1536;    // ints: 1024 tokens + ancestors (p >= 4)
+
+struct FastBuf {
+  float r0[kFastU][kE];            // level-0 rows (zero when not selected)
+  int s0[kFastU];
+  float ri[kFastInner][kE];        // inner-level rows that change at the chunk start
+  int si[kFastInner];
+};
+
+template <typename Tout>
+__global__ __launch_bounds__(256) void bcast_fast(BcastArgs a) {
+  const Geo& g = a.g;
+  const int lpr = g.d / kE;
+  const int rgs = 256 / lpr;
+  const int BT = rgs * kFastTok;  // tokens per workgroup
+  const int rg = threadIdx.x / lpr, lane = threadIdx.x % lpr;
+  const int64_t bh = blockIdx.y;
+  const int z = blockIdx.z;
+  const int32_t B0 = (int32_t)blockIdx.x * BT;
+  const int32_t* pos = a.pos + bh * g.M;
+  const int lg = g.log2p;
+  __shared__ int32_t sp[kPosCache];
+  __shared__ int32_t soff[kMaxLevels];  // start of level l's run in sp
+
+  // ---- stage positions: tokens [B0, B0 + BT), then each level's ancestors
+  for (int i = threadIdx.x; i < BT; i += 256) sp[i] = B0 + i < g.N ? pos[B0 + i] : -1;
+  const int lbt = __builtin_ctz(BT);  // BT is a power of two (64 tokens x 8 or 16 row groups)
+  int off = BT;
+  for (int l = 1; l < g.L; ++l) {
+    const int n = lg * l >= lbt ? 1 : BT >> (lg * l);  // ancestors of the block: max(1, BT / p^l)
+    const int32_t jlo = B0 >> (lg * l);
+    if (threadIdx.x == 0) soff[l] = off;
+    for (int i = threadIdx.x; i < n; i += 256)
+      sp[off + i] = jlo + i < g.nlev[l] ? pos[g.base[l] + jlo + i] : -1;
+    off += n;
+  }
+  __syncthreads();
+  const int32_t t0 = B0 + rg * kFastTok;
+  if (t0 >= g.N) return;  // no barrier below
+  const int32_t t1 = min(t0 + kFastTok, g.N);
+
+  const float* src = a.src[z] + bh * (int64_t)g.S * g.d + kE * lane;
+  Tout* out = static_cast<Tout*>(a.out[z]) + bh * (int64_t)g.N * g.d + kE * lane;
+  const bool mean = a.mean != 0;
+
+  // levels 1 .. lam-1 are inner (p^l < 64), lam .. L-1 outer
+  int lam = 1;
+  while (lam < g.L && (lg * lam) < 6) ++lam;
+  const int nin = lam - 1;  // <= 2 since p >= 4
+
+  auto level_pos = [&](int l, int32_t j) { return sp[soff[l] + (j - (B0 >> (lg * l)))]; };
+  auto load_row = [&](int32_t r, float (&x)[kE]) {
+    const f32x4 q = *reinterpret_cast<const f32x4*>(src + (int64_t)r * g.d);
+#pragma unroll
+    for (int e = 0; e < kE; ++e) x[e] = q[e];
+  };
+
+  // ---- outer levels: the same ancestors for all 64 tokens of the group
+  float A[kFastInner + 1][kE];  // A[k]: sum over levels >= k+1 ... A[nin]: outer
+  int C[kFastInner + 1];
+  {
+    float rows[kFastOuter][kE];
+    int sel[kFastOuter];
+#pragma unroll
+    for (int k = 0; k < kFastOuter; ++k) {
+      const int l = lam + k;
+      sel[k] = 0;
+#pragma unroll
+      for (int e = 0; e < kE; ++e) rows[k][e] = 0.f;
+      if (l < g.L) {
+        const int32_t pe = level_pos(l, t0 >> (lg * l));
+        if (pe >= 0) {
+          load_row(pe, rows[k]);
+          sel[k] = 1;
+        }
+      }
+    }
+    float acc[kE] = {0.f, 0.f, 0.f, 0.f};
+    int cnt = 0;
+#pragma unroll
+    for (int k = 0; k < kFastOuter; ++k) {
+      const float w = mean ? 1.0f : g.inv_pw[min(lam + k, kMaxLevels - 1)];
+#pragma unroll
+      for (int e = 0; e < kE; ++e) acc[e] += rows[k][e] * w;
+      cnt += sel[k];
+    }
+    for (int l = lam + kFastOuter; l < g.L; ++l) {  // very deep pyramids: one at a time
+      const int32_t pe = level_pos(l, t0 >> (lg * l));
+      if (pe >= 0) {
+        float x[kE];
+        load_row(pe, x);
+        const float w = mean ? 1.0f : g.inv_pw[l];
+#pragma unroll
+        for (int e = 0; e < kE; ++e) acc[e] += x[e] * w;
+        ++cnt;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k <= kFastInner; ++k) {
+      C[k] = cnt;
+#pragma unroll
+      for (int e = 0; e < kE; ++e) A[k][e] = acc[e];
+    }
+  }
+
+  // ---- chunk pipeline over the group's tokens
+  auto issue = [&](int32_t c, FastBuf& b) {
+#pragma unroll
+    for (int u = 0; u < kFastU; ++u) {
+      const int32_t t = c + u;
+      const int32_t p0 = t < t1 ? sp[t - B0] : -1;
+      b.s0[u] = p0 >= 0;
+#pragma unroll
+      for (int e = 0; e < kE; ++e) b.r0[u][e] = 0.f;
+      if (p0 >= 0) load_row(p0, b.r0[u]);
+    }
+#pragma unroll
+    for (int k = 0; k < kFastInner; ++k) {
+      const int l = k + 1;
+      b.si[k] = 0;
+#pragma unroll
+      for (int e = 0; e < kE; ++e) b.ri[k][e] = 0.f;
+      if (l <= nin && (c & ((1 << (lg * l)) - 1)) == 0) {
+        const int32_t pe = level_pos(l, c >> (lg * l));
+        if (pe >= 0) {
+          load_row(pe, b.ri[k]);
+          b.si[k] = 1;
+        }
+      }
+    }
+  };
+  auto process = [&](int32_t c, const FastBuf& b) {
+    // inner levels that change at c, top down: A[l-1] = A[l] + row_l (A[nin] = outer)
+#pragma unroll
+    for (int k = kFastInner - 1; k >= 0; --k) {
+      const int l = k + 1;
+      if (l <= nin && (c & ((1 << (lg * l)) - 1)) == 0) {
+        const float w = mean ? 1.0f : g.inv_pw[l];
+        C[k] = C[k + 1] + b.si[k];
+#pragma unroll
+        for (int e = 0; e < kE; ++e) A[k][e] = A[k + 1][e] + b.ri[k][e] * w;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kFastU; ++u) {
+      const int32_t t = c + u;
+      if (t >= t1) break;
+      const float rc = mean ? 1.0f / static_cast<float>(C[0] + b.s0[u]) : 1.0f;
+      float o[kE];
+#pragma unroll
+      for (int e = 0; e < kE; ++e) o[e] = (A[0][e] + b.r0[u][e]) * rc;
+      Out4<Tout>::store(out + (int64_t)t * g.d, o);
+    }
+  };
+  if (nin == 0) {  // A[0] must be the outer sum
+#pragma unroll
+    for (int e = 0; e < kE; ++e) A[0][e] = A[kFastInner][e];
+    C[0] = C[kFastInner];
+  } else if (nin == 1) {  // A[1] plays the outer sum for level 1
+#pragma unroll
+    for (int e = 0; e < kE; ++e) A[1][e] = A[kFastInner][e];
+    C[1] = C[kFastInner];
+  }
+  FastBuf ba, bb;
+  issue(t0, ba);
+  for (int32_t c = t0; c < t1; c += 2 * kFastU) {
+    if (c + kFastU < t1) issue(c + kFastU, bb);
+    process(c, ba);
+    if (c + kFastU >= t1) break;
+    if (c + 2 * kFastU < t1) issue(c + 2 * kFastU, ba);
+    process(c + kFastU, bb);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_bcast(const BcastArgs& a, int dtype, int ntensors, int64_t BH, hipStream_t st) {
   const int rgs = 256 / (a.g.d / kE);
+  if (LH_BC_FAST && a.g.log2p >= 2) {
+    const int64_t bt = (int64_t)rgs * kFastTok;
+    const dim3 grid((unsigned)((a.g.N + bt - 1) / bt), (unsigned)BH, (unsigned)ntensors);
+    if (dtype == 1) bcast_fast<__bf16><<<grid, 256, 0, st>>>(a);
+    else bcast_fast<float><<<grid, 256, 0, st>>>(a);
+    return hipGetLastError();
+  }
   const int64_t per_block = (int64_t)rgs * kTokPerGroup;
   const dim3 grid((unsigned)((a.g.N + per_block - 1) / per_block), (unsigned)BH);
   if (dtype == 1) {
