@@ -58,6 +58,7 @@ lh_status make_plan(const lh_shape* s, Plan& P) {
     return fail(LH_EINVAL, "B, H, N and d must be positive");
   if (s->dtype != LH_FP32 && s->dtype != LH_BF16) return fail(LH_EINVAL, "unknown dtype");
   if (s->p < 2) return fail(LH_EINVAL, "pooling factor p must be >= 2");
+  if (s->p > 64) return fail(LH_EUNSUPPORTED, "pooling factor p > 64 is not supported");
   if (s->L < 1) return fail(LH_EINVAL, "L must be >= 1");
   if (s->L > lh::kMaxLevels) return fail(LH_EUNSUPPORTED, "L > 16 levels is not supported");
   if (s->d != 64 && s->d != 128) return fail(LH_EUNSUPPORTED, "head dim must be 64 or 128");

@@ -199,7 +199,12 @@ __global__ __launch_bounds__(256) void pool_fwd_kernel(PoolFwdArgs a, int do_poo
 // Scatter backward: dos[pos(e)] = sum over tokens t of e's span of
 // dout[t] / c_t.  Same row-group walk as the forward; only selected entries
 // are written.  On the token pass, c_t (the number of selected ancestors of
-// t) comes from an ancestor walk that keeps per-level counts.
+// t) comes from an ancestor walk that keeps per-level counts.  The positions
+// the workgroup needs (its rows' own, the levels it writes and, on the token
+// pass, every ancestor level) are first staged in LDS in one coalesced
+// burst, so that no load of a row group waits on a position load.
+constexpr int kBwdPosCache = 4608;  // ints: workgroup rows + their ancestors (p >= 2)
+
 template <typename Tin, typename Tout, bool FIRST>
 __global__ __launch_bounds__(256) void pool_bwd_kernel(PoolBwdArgs a) {
   const Geo& g = a.g;
@@ -210,13 +215,40 @@ __global__ __launch_bounds__(256) void pool_bwd_kernel(PoolBwdArgs a) {
   const int64_t bh = blockIdx.y;
   const int64_t nchunks = (a.in_rows + a.chunk - 1) / a.chunk;
   const int64_t c = (int64_t)blockIdx.x * rgs + rg;
-  if (c >= nchunks) return;
+  const int32_t* pos = a.pos + bh * g.M;
+
+  // ---- stage positions: rows [B0, B0 + BT) of level lvl0 (token pass), then
+  // the entries of every level above lvl0 that these rows belong to
+  __shared__ int32_t sp[kBwdPosCache];
+  __shared__ int32_t soff[kMaxLevels], sjlo[kMaxLevels];
+  const int64_t B0 = (int64_t)blockIdx.x * rgs * a.chunk;
+  const int64_t BT = min((int64_t)rgs * a.chunk, a.in_rows - B0);
+  int off = 0;
+  if (FIRST) {
+    for (int i = threadIdx.x; i < BT; i += 256) sp[i] = pos[B0 + i];
+    off = (int)BT;
+  }
+  const int ltop = FIRST ? g.L : min(g.L, a.lvl0 + a.lam + 1);  // levels whose positions are read
+  for (int l = a.lvl0 + 1; l < ltop; ++l) {
+    const int32_t f = g.pw[l] / g.pw[a.lvl0];  // rows of level lvl0 per entry of level l
+    const int32_t jlo = (int32_t)(B0 / f);
+    const int32_t jhi = (int32_t)((B0 + BT - 1) / f);
+    if (threadIdx.x == 0) {
+      soff[l] = off;
+      sjlo[l] = jlo;
+    }
+    for (int i = threadIdx.x; i <= jhi - jlo; i += 256) sp[off + i] = pos[g.base[l] + jlo + i];
+    off += jhi - jlo + 1;
+  }
+  __syncthreads();
+  if (c >= nchunks) return;  // no barrier below
+  auto posf = [&](int l, int32_t j) { return sp[soff[l] + (j - sjlo[l])]; };
+
   const int64_t r0 = c * a.chunk;
   const int nrows = (int)min((int64_t)a.chunk, a.in_rows - r0);
   const Tin* in = static_cast<const Tin*>(a.in) + bh * a.in_rows * d + 8 * lane;
   Tout* dos = static_cast<Tout*>(a.dos) + bh * (int64_t)g.S * d + 8 * lane;
   float* so = a.sums_out ? a.sums_out + bh * a.out_rows * d + 8 * lane : nullptr;
-  const int32_t* pos = a.pos + bh * g.M;
 
   float acc[kStageLevels][8];
   int cnt[kStageLevels];
@@ -234,14 +266,14 @@ __global__ __launch_bounds__(256) void pool_bwd_kernel(PoolBwdArgs a) {
     for (int u = 0; u < kRowsInFlight; ++u) {
       const int64_t row = r0 + min(rb + u, nrows - 1);
       Row8<Tin>::template load<kStream>(in + row * d, xs[u]);
-      if constexpr (FIRST) pt[u] = pos[row];
+      if constexpr (FIRST) pt[u] = sp[row - B0];
     }
 #pragma unroll
     for (int u = 0; u < kRowsInFlight; ++u) {
       if (rb + u >= nrows) break;
       const int64_t row = r0 + rb + u;
       if constexpr (FIRST) {
-        walk.advance((int32_t)row, pos, nullptr, g, true, lane);
+        walk.advance((int32_t)row, posf, nullptr, g, true, lane);
         const int ct = walk.cnt[1] + (pt[u] >= 0 ? 1 : 0);
         const float rc = 1.0f / static_cast<float>(ct);
 #pragma unroll
@@ -257,7 +289,7 @@ __global__ __launch_bounds__(256) void pool_bwd_kernel(PoolBwdArgs a) {
         cnt[l] = 0;
         const int lev = a.lvl0 + l + 1;
         const int64_t j = (row + 1) / g.pw[l + 1] - 1;
-        const int32_t pe = pos[g.base[lev] + j];
+        const int32_t pe = posf(lev, (int32_t)j);
         if (pe >= 0) Row8<Tout>::store(dos + (int64_t)pe * d, acc[l]);
         if (l + 1 < kStageLevels && l + 1 < a.lam) {
 #pragma unroll

@@ -95,7 +95,7 @@ __global__ __launch_bounds__(256) void bcast_kernel(BcastArgs a) {
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       if (t + u >= t1) break;
-      w.advance(t + u, pos, src, g, mean, lane);
+      w.advance(t + u, [&](int l, int32_t j) { return pos[g.base[l] + j]; }, src, g, mean, lane);
       const int c = w.cnt[1] + (r0[u] >= 0 ? 1 : 0);
       const float rc = mean ? 1.0f / static_cast<float>(c) : 1.0f;
 #pragma unroll

@@ -31,10 +31,12 @@ struct AncestorWalk {
   int cnt[kTop + 1];
   bool started = false;
 
+  // posf(l, j): subsequence position of entry j of level l (-1: not selected)
+  template <typename PosF>
   __device__ __forceinline__ void add_entry(float (&acc)[kNT][E], int& c, int l, int32_t j,
-                                            const int32_t* pos, const float* const* src,
+                                            const PosF& posf, const float* const* src,
                                             const Geo& g, bool mean, int lane) {
-    const int32_t r = pos[g.base[l] + j];
+    const int32_t r = posf(l, j);
     if (r < 0) return;
     ++c;
     if constexpr (NT > 0) {
@@ -61,12 +63,13 @@ struct AncestorWalk {
   }
 
   // Bring the level sums up to date for token t.
-  __device__ __forceinline__ void advance(int32_t t, const int32_t* pos, const float* const* src,
+  template <typename PosF>
+  __device__ __forceinline__ void advance(int32_t t, const PosF& posf, const float* const* src,
                                           const Geo& g, bool mean, int lane) {
     if (!started || (g.L > kTop && on_boundary(t, g, kTop))) {
       clear(kTop);
       for (int l = kTop; l < g.L; ++l)
-        add_entry(A[kTop], cnt[kTop], l, div_pw(t, g, l), pos, src, g, mean, lane);
+        add_entry(A[kTop], cnt[kTop], l, div_pw(t, g, l), posf, src, g, mean, lane);
     }
 #pragma unroll
     for (int l = kWalkLevels; l >= 1; --l) {
@@ -76,7 +79,7 @@ struct AncestorWalk {
       for (int i = 0; i < kNT; ++i)
 #pragma unroll
         for (int e = 0; e < E; ++e) A[l][i][e] = A[l + 1][i][e];
-      if (l < g.L) add_entry(A[l], cnt[l], l, div_pw(t, g, l), pos, src, g, mean, lane);
+      if (l < g.L) add_entry(A[l], cnt[l], l, div_pw(t, g, l), posf, src, g, mean, lane);
     }
     started = true;
   }

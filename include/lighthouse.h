@@ -34,8 +34,10 @@
  *    lh_last_error() gives a message for the calling thread.
  *  - Determinism: identical inputs give bit-identical outputs (no floating
  *    point atomics anywhere).
- *  - Shape limits: p >= 2, 1 <= L <= 16, N % p^(L-1) == 0,
- *    n_coarse <= S <= M, d in {64, 128}, B*H*M < 2^31.
+ *  - Shape limits: 2 <= p <= 64, 1 <= L <= 16, N % p^(L-1) == 0,
+ *    n_coarse <= S <= M, d in {64, 128}, B*H*M < 2^31 (p > 64 returns
+ *    LH_EUNSUPPORTED: the pooling kernels stage a workgroup's positions in
+ *    LDS sized for spans of at most 64 rows per pass).
  */
 #ifndef LIGHTHOUSE_H
 #define LIGHTHOUSE_H

@@ -56,6 +56,7 @@ def test_sizes_match_geometry(lb, N, p, L, S):
     ((1, 1, 64, 64, 4, 3, 3, 1), 1),          # S below the coarsest level
     ((1, 1, 64, 64, 4, 3, 85, 1), 1),         # S above M
     ((1, 1, 64, 64, 1, 3, 20, 1), 1),         # p < 2
+    ((1, 1, 65 * 65, 64, 65, 3, 80, 1), 2),   # p > 64
     ((1, 1, 64, 64, 4, 0, 20, 1), 1),         # L < 1
     ((1, 1, 1 << 17, 64, 2, 17, 20, 1), 2),   # too many levels
     ((1, 1, 64, 64, 4, 3, 20, 7), 1),         # unknown dtype
