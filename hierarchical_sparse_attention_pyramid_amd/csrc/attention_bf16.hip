@@ -391,26 +391,28 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void attn_fwd_bf16(
     const uint32_t lk = lrow ^ kbo;
     const uint32_t lv = ltr ^ (kbo + C::kTile * 2);
 
+    // Issue every LDS read of this tile before the first MFMA that needs it
+    // (the V^T operands do not depend on the scores, so their latency hides
+    // under the QK^T products and the softmax); with two query blocks per
+    // wave both use the same operands, which halves LDS traffic per product.
+    bf16x8 kop[2][D / 16];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int dc = 0; dc < D / 16; ++dc) kop[kb][dc] = lds_rows<D>(sKV, lk, kb * 32, dc);
+    bf16x8 vop[2][2][D / 32];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int mb = 0; mb < D / 32; ++mb)
+          vop[kb][c][mb] = lds_tr8<D>(sKV, lv, kb * 32 + 16 * c, mb * 32);
+
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
       const int qbase = qw0 + qb * 32;
       if (k0 > qbase + 31) continue;
-      // Issue every LDS read of this step before the first MFMA that needs
-      // it: the V^T operands do not depend on the scores, so their latency
-      // hides under the QK^T products and the softmax.
-      bf16x8 kop[2][D / 16];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int dc = 0; dc < D / 16; ++dc) kop[kb][dc] = lds_rows<D>(sKV, lk, kb * 32, dc);
-      bf16x8 vop[2][2][D / 32];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int c = 0; c < 2; ++c)
-#pragma unroll
-          for (int mb = 0; mb < D / 32; ++mb)
-            vop[kb][c][mb] = lds_tr8<D>(sKV, lv, kb * 32 + 16 * c, mb * 32);
       f32x16 sacc[2] = {zero16(), zero16()};
 #pragma unroll
       for (int dc = 0; dc < D / 16; ++dc)

@@ -33,20 +33,37 @@ namespace {
 constexpr int kRowsInFlight = LH_POOL_ROWS;  // rows whose loads a row group issues together
 constexpr bool kStream = LH_POOL_NT != 0;    // token rows are read once: streaming loads
 
+// y[lane + k] for lanes of the same 16-lane DPP row (row_shl:k); used only
+// where lane + k stays inside the lane's row group.
+template <int K>
+__device__ __forceinline__ float from_lane_plus(float y) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, y), 0x100 + K,
+                                                            0xf, 0xf, true));
+}
+
 // ||x||_2 of a d-long row spread over `lpr` lanes (element 8*lane + e in
 // x[e]), in the fixed float32 order: squares, then the halving tree
 // y[i] += y[i + w/2] for w = d, d/2, ..., 2 (cross-lane strides d/2..8 first,
 // then in-lane strides 4, 2, 1), then a correctly rounded square root.  No
-// fused multiply-add, so the result is reproducible bit for bit.
+// fused multiply-add, so the result is reproducible bit for bit.  The value
+// is exact in the row group's first lane (the one that uses it); the
+// cross-lane steps shift lanes down (DPP row_shl) toward that lane, so no
+// LDS crossbar traffic is needed.
 __device__ __forceinline__ float row_norm(const float (&x)[8], int lpr) {
 #pragma clang fp contract(off)
   float a[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) a[e] = x[e] * x[e];
-  for (int off = lpr >> 1; off >= 1; off >>= 1) {
+  if (lpr == 16) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) a[e] = a[e] + __shfl_xor(a[e], off);
+    for (int e = 0; e < 8; ++e) a[e] = a[e] + from_lane_plus<8>(a[e]);
   }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) a[e] = a[e] + from_lane_plus<4>(a[e]);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) a[e] = a[e] + from_lane_plus<2>(a[e]);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) a[e] = a[e] + from_lane_plus<1>(a[e]);
   const float b0 = a[0] + a[4], b1 = a[1] + a[5], b2 = a[2] + a[6], b3 = a[3] + a[7];
   const float c0 = b0 + b2, c1 = b1 + b3;
   return sqrtf(c0 + c1);  // correctly rounded on gfx950 (not __fsqrt_rn)
@@ -258,6 +275,16 @@ __global__ __launch_bounds__(256) void pool_bwd_kernel(PoolBwdArgs a) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[l][e] = 0.f;
   }
+  // c_t on the token pass.  p a power of two >= 4: the row group is 64
+  // aligned rows, so levels with p^l >= 64 give the same count to all of its
+  // rows (counted once here) and at most two inner levels vary per row.
+  // Other p: the ancestor walk of counts.
+  const bool fastc = FIRST && g.log2p >= 2;
+  int cnt_outer = 0;
+  if (fastc) {
+    for (int l = 1; l < g.L; ++l)
+      if (g.log2p * l >= 6) cnt_outer += posf(l, (int32_t)(r0 >> (g.log2p * l))) >= 0;
+  }
   AncestorWalk<0, 1> walk;
   for (int rb = 0; rb < nrows; rb += kRowsInFlight) {
     float xs[kRowsInFlight][8];
@@ -273,8 +300,16 @@ __global__ __launch_bounds__(256) void pool_bwd_kernel(PoolBwdArgs a) {
       if (rb + u >= nrows) break;
       const int64_t row = r0 + rb + u;
       if constexpr (FIRST) {
-        walk.advance((int32_t)row, posf, nullptr, g, true, lane);
-        const int ct = walk.cnt[1] + (pt[u] >= 0 ? 1 : 0);
+        int ct = (pt[u] >= 0 ? 1 : 0);
+        if (fastc) {
+          ct += cnt_outer;
+#pragma unroll
+          for (int l = 1; l <= 2; ++l)
+            if (l < g.L && g.log2p * l < 6) ct += posf(l, (int32_t)(row >> (g.log2p * l))) >= 0;
+        } else {
+          walk.advance((int32_t)row, posf, nullptr, g, true, lane);
+          ct += walk.cnt[1];
+        }
         const float rc = 1.0f / static_cast<float>(ct);
 #pragma unroll
         for (int e = 0; e < 8; ++e) xs[u][e] *= rc;
