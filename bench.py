@@ -9,9 +9,17 @@ of synthetic input already resident in HBM.  The headline workload is the
   * the 524,288-token layer (H=16, d=128, p=4, L=6, S=16384) forward and
     forward+backward, against the same-GPU dense causal attention (the same
     attention kernels at S = N);
-  * the CPU oracle timed on one head of the headline workload (cpu_baseline).
+  * the CPU oracle timed on one head of the headline workload (cpu_baseline),
+    plus single-thread oracle times on the two small workloads;
+  * each stage's fraction of measured ceilings as well as of the datasheet
+    peaks: a 1 GiB device copy (HBM) and a large bf16 GEMM (matrix cores);
+  * `extras`: the other workload shapes (32K forward, the degenerate S = N
+    2K forward, 1M forward+backward) and the pages' own operating points
+    (L = 3, S = N/p^2 + 1536 for p = 4 and 2 at 98K and 512K, p = 4 at 1M),
+    throughput only; the operating points reuse the inputs of the workload
+    with the same N, H and d.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-long] [--no-cpu]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-long] [--no-cpu] [--no-extras]
 Prints one JSON line on stdout; progress goes to stderr.
 """
 from __future__ import annotations
@@ -137,6 +145,21 @@ class Layer:
         self.ws = lb.workspace(max(z.ws_forward, z.ws_backward))
         self.lb = lb
 
+    @classmethod
+    def sharing(cls, other, cfg, torch, lb):
+        """A layer of another (p, L, S) on the same input tensors (same B, H, N, d)."""
+        lay = cls.__new__(cls)
+        lay.cfg, lay.x, lay.lb = cfg, other.x, lb
+        lay.shape = lb.make_shape(cfg.B, cfg.H, cfg.N, cfg.d, cfg.p, cfg.L, cfg.S,
+                                  other.x["q"].dtype)
+        lay.bufs = lb.LayerBuffers(lay.shape)
+        lay.z = lay.bufs.sizes
+        lay.out = other.out
+        if cfg.backward:
+            lay.dq, lay.dk, lay.dv = other.dq, other.dk, other.dv
+        lay.ws = lb.workspace(max(lay.z.ws_forward, lay.z.ws_backward))
+        return lay
+
     def forward(self):
         x = self.x
         self.lb.lh_forward(self.shape, x["q"], x["k"], x["v"], self.out, self.bufs, self.ws)
@@ -163,6 +186,22 @@ def time_fn(torch, fn, steps, warmup):
     b.record()
     torch.cuda.synchronize()
     return a.elapsed_time(b) / steps
+
+
+def measured_ceilings(torch):
+    """Practical ceilings on this GPU: a 1 GiB device-to-device copy (GB/s,
+    read + write bytes) and a 8192^3 bf16 GEMM through torch (TFLOP/s)."""
+    a = torch.ones(256 << 20, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    t_copy = time_fn(torch, lambda: b.copy_(a), 10, 2)
+    del a, b
+    x = torch.randn(8192, 8192, device="cuda").to(torch.bfloat16)
+    y = torch.randn(8192, 8192, device="cuda").to(torch.bfloat16)
+    t_mm = time_fn(torch, lambda: torch.matmul(x, y), 10, 3)
+    del x, y
+    torch.cuda.empty_cache()
+    return {"copy_GBs": round(2 * (1 << 30) / (t_copy * 1e-3) / 1e9, 1),
+            "gemm_bf16_TFLOPs": round(2 * 8192 ** 3 / (t_mm * 1e-3) / 1e12, 1)}
 
 
 def calibration_copy(torch):
@@ -204,6 +243,40 @@ def dense_times(torch, lb, lay, steps, warmup):
     return t_f, t_fb, flops_f
 
 
+def throughput(torch, lay, steps):
+    """Forward (and forward+backward where the workload has one) throughput."""
+    cfg = lay.cfg
+    r = {"workload": cfg.name, "N": cfg.N, "H": cfg.H, "d": cfg.d, "p": cfg.p, "L": cfg.L,
+         "S": cfg.S}
+    t_f = time_fn(torch, lay.forward, steps, 1)
+    r["fwd_ms"] = round(t_f, 3)
+    r["fwd_tokens_per_s"] = round(cfg.B * cfg.N / (t_f * 1e-3), 1)
+    if cfg.backward:
+        t_fb = time_fn(torch, lay.step, steps, 1)
+        r["fwdbwd_ms"] = round(t_fb, 3)
+        r["fwdbwd_tokens_per_s"] = round(cfg.B * cfg.N / (t_fb * 1e-3), 1)
+    log(f"[bench] extra {cfg.name}: " + ", ".join(f"{k}={v}" for k, v in r.items()
+                                                  if k.endswith("_ms")))
+    return r
+
+
+def cpu_single_thread(names):
+    """Single-thread oracle forward time on the first head of small workloads."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import lighthouse as O
+    from synth import inputs as synth
+    out = {}
+    with threadpool_limits(limits=1):
+        for name in names:
+            cfg = synth.CONFIGS[name]
+            x = synth.make_inputs(cfg, tensors=("q", "k", "v"), heads=[(0, 0)])
+            t0 = time.perf_counter()
+            O.forward_head(x["q"][0], x["k"][0], x["v"][0], cfg.p, cfg.L, cfg.S, cfg.dtype)
+            out[name] = {"fwd_s_one_head": round(time.perf_counter() - t0, 3), "threads": 1}
+    return out
+
+
 def cpu_baseline(cfg):
     """The oracle as it stands, on one head of the headline workload, scaled to
     the whole layer (all B*H heads)."""
@@ -233,6 +306,8 @@ def main():
     ap.add_argument("--dense-steps", type=int, default=2)
     ap.add_argument("--no-long", action="store_true", help="skip the 512K comparison")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the other workload shapes and the pages' operating points")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -246,6 +321,8 @@ def main():
     lb.load_library()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     calibration_copy(torch)
+    ceil = measured_ceilings(torch)
+    log(f"[bench] measured ceilings: {ceil}")
 
     cfg = synth.CONFIGS[HEADLINE]
     lay = Layer(cfg, torch, lb)
@@ -260,6 +337,8 @@ def main():
     for k, t in stages_ms.items():
         kind, w = work[k]
         stages[k] = {"ms": round(t, 4), **roofline_entry(kind, w, t, cfg.dtype)}
+        meas = ceil["copy_GBs"] if kind == "hbm" else ceil["gemm_bf16_TFLOPs"]
+        stages[k]["frac_measured"] = round(stages[k]["achieved"] / meas, 4)
     dom = max((k for k in stages_ms if k in KERNEL_OF_STAGE), key=lambda k: stages_ms[k])
     kname, kfile = KERNEL_OF_STAGE[dom]
     kind, w = work[dom]
@@ -267,6 +346,12 @@ def main():
     roof["kernel"] = kname
     roof["traffic"] = measured_traffic(kname, kfile)
     log(f"[bench] stages (ms): " + ", ".join(f"{k}={v:.4f}" for k, v in stages_ms.items()))
+    extras = []
+    if not args.no_extras:
+        for name in ("op_n98k_p4_bf16", "op_n98k_p2_bf16"):
+            e = Layer.sharing(lay, synth.CONFIGS[name], torch, lb)
+            extras.append(throughput(torch, e, 5))
+            del e
     del lay
     torch.cuda.empty_cache()
 
@@ -289,12 +374,32 @@ def main():
             "dense_fwd_tflops": round(d_flops / (d_f * 1e-3) / 1e12, 1),
             "speedup_fwd": round(d_f / l_f, 2), "speedup_fwdbwd": round(d_fb / l_fb, 2),
         }
+        if not args.no_extras:
+            for name in ("op_n512k_p4_bf16", "op_n512k_p2_bf16"):
+                e = Layer.sharing(ll, synth.CONFIGS[name], torch, lb)
+                extras.append(throughput(torch, e, 3))
+                del e
         del ll
+        torch.cuda.empty_cache()
+
+    if not args.no_extras:
+        for name in ("fwd_n32k_bf16", "dense_n2k_bf16"):
+            e = Layer(synth.CONFIGS[name], torch, lb, backward=False)
+            extras.append(throughput(torch, e, 10))
+            del e
+            torch.cuda.empty_cache()
+        big = Layer(synth.CONFIGS["long_n1m_bf16"], torch, lb)
+        extras.append(throughput(torch, big, 3))
+        e = Layer.sharing(big, synth.CONFIGS["op_n1m_p4_bf16"], torch, lb)
+        extras.append(throughput(torch, e, 2))
+        del e, big
         torch.cuda.empty_cache()
 
     cpu = None if args.no_cpu else cpu_baseline(cfg)
     if cpu:
         log(f"[bench] cpu oracle: {cpu['value']} tokens/s ({cpu['sample']})")
+        cpu["single_thread"] = cpu_single_thread(("fwd_n4k_fp32", "fwd_n32k_bf16"))
+        log(f"[bench] cpu oracle, one thread: {cpu['single_thread']}")
 
     rec = {
         "metric": METRIC,
@@ -315,7 +420,9 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "stages": stages,
+        "measured_ceilings": ceil,
         "long_context": long_ctx,
+        "extras": extras,
     }
     print(json.dumps(rec), flush=True)
 
