@@ -13,7 +13,8 @@ of synthetic input already resident in HBM.  The headline workload is the
     plus single-thread oracle times on the two small workloads;
   * each stage's fraction of measured ceilings as well as of the datasheet
     peaks: a 1 GiB device copy (HBM) and a large bf16 GEMM (matrix cores);
-  * `extras`: the other workload shapes (32K forward, the degenerate S = N
+  * `extras`: the layer inside an attention block with Q/K/V/O projections
+    (autograd, D = H*d) at the headline shape; the other workload shapes (32K forward, the degenerate S = N
     2K forward, 1M forward+backward) and the pages' own operating points
     (L = 3, S = N/p^2 + 1536 for p = 4 and 2 at 98K and 512K, p = 4 at 1M),
     throughput only; the operating points reuse the inputs of the workload
@@ -260,6 +261,37 @@ def throughput(torch, lay, steps):
     return r
 
 
+def block_throughput(torch, cfg, steps):
+    """The layer inside an attention block (Q/K/V and output projections,
+    autograd through lh_forward / lh_backward), model width D = H * d, at the
+    workload's shape; forward+backward including the projection GEMMs."""
+    from hierarchical_sparse_attention_pyramid_amd.layer import LighthouseAttention
+    from synth import inputs as synth
+    D = cfg.H * cfg.d
+    m = LighthouseAttention(D, cfg.H, cfg.d, cfg.p, cfg.L, cfg.S)
+    x = torch.from_numpy(synth.block_tensor(900, (cfg.B * cfg.N, D), "bf16").view("int16"))
+    x = x.view(torch.bfloat16).cuda().view(cfg.B, cfg.N, D).requires_grad_(True)
+    dy = torch.randn(cfg.B, cfg.N, D, device="cuda").to(torch.bfloat16)
+
+    def step():
+        for t in (x, m.wq, m.wk, m.wv, m.wo):
+            t.grad = None
+        m(x).backward(dy)
+
+    t = time_fn(torch, step, steps, 2)
+    with torch.no_grad():
+        t_f = time_fn(torch, lambda: m(x), steps, 1)
+    gemm_flops = 3 * 2 * 4 * cfg.B * cfg.N * D * D  # 4 projections, forward + two backward GEMMs each
+    r = {"workload": f"block_{cfg.name}", "D": D, "H": cfg.H, "d": cfg.d, "N": cfg.N, "p": cfg.p,
+         "L": cfg.L, "S": cfg.S, "fwd_ms": round(t_f, 3), "fwdbwd_ms": round(t, 3),
+         "fwdbwd_tokens_per_s": round(cfg.B * cfg.N / (t * 1e-3), 1),
+         "projection_gemm_tflop": round(gemm_flops / 1e12, 3)}
+    log(f"[bench] block {cfg.name}: forward {t_f:.3f} ms, forward+backward {t:.3f} ms")
+    del m, x, dy
+    torch.cuda.empty_cache()
+    return r
+
+
 def cpu_single_thread(names):
     """Single-thread oracle forward time on the first head of small workloads."""
     from threadpoolctl import threadpool_limits
@@ -383,6 +415,7 @@ def main():
         torch.cuda.empty_cache()
 
     if not args.no_extras:
+        extras.append(block_throughput(torch, synth.CONFIGS[HEADLINE], 10))
         for name in ("fwd_n32k_bf16", "dense_n2k_bf16"):
             e = Layer(synth.CONFIGS[name], torch, lb, backward=False)
             extras.append(throughput(torch, e, 10))

@@ -111,6 +111,13 @@ def head_tensor(cfg_seed: int, tensor: str, b: int, h: int, N: int, d: int,
     return z
 
 
+def block_tensor(seed: int, shape, dtype: str, scale: float = 1.0) -> np.ndarray:
+    """Seeded N(0, scale^2) tensor in storage form (block inputs and projection
+    weights of the attention-block tests): float32 draws, bf16 rounded once."""
+    x = np.random.default_rng(seed).standard_normal(shape, dtype=np.float32) * np.float32(scale)
+    return bf16_bits_from_f32(x) if dtype == "bf16" else x
+
+
 def _head_storage(args):
     cfg_seed, tensor, b, h, N, d, planted, dtype = args
     x = head_tensor(cfg_seed, tensor, b, h, N, d, planted)
