@@ -189,34 +189,50 @@ __global__ __launch_bounds__(kThreads) void topk_scan(void* ws, int64_t nblk) {
   }
 }
 
+// Ordered compaction of one block's slice: thread t owns the contiguous
+// candidates i0 + 16t .. i0 + 16t + 15, so two block scans (equal-to-T ranks,
+// then output offsets) order the whole slice.
 __global__ __launch_bounds__(kThreads) void topk_write(const float* score, int32_t* sel, void* ws,
                                                        int64_t nblk, int32_t M, int32_t C,
                                                        int32_t K) {
+  constexpr int kPer = kSlice / kThreads;
   __shared__ uint32_t sh[kThreads / 64];
   const int64_t bh = blockIdx.y;
-  uint32_t* w = head_ws(ws, bh, nblk);
+  const uint32_t* w = head_ws(ws, bh, nblk);
   const uint32_t T = w[0], need = w[1];
   const uint32_t* blk = w + 4 + kBins;
-  uint32_t off = blk[2 * nblk + blockIdx.x];
-  uint32_t eqb = blk[3 * nblk + blockIdx.x];
+  const uint32_t off = blk[2 * nblk + blockIdx.x];
+  const uint32_t eqb = blk[3 * nblk + blockIdx.x];
   const float* s = score + bh * M;
   int32_t* out = sel + bh * K;
-  const int i0 = blockIdx.x * kSlice;
-  const int i1 = min(i0 + kSlice, C);
-  for (int base = i0; base < i1; base += kThreads) {
-    const int i = base + threadIdx.x;
-    const bool valid = i < i1;
-    const uint32_t u = valid ? __float_as_uint(s[i]) : 0u;
-    const bool is_gt = valid && u > T;
-    const bool is_eq = valid && u == T;
-    uint32_t eq_total;
-    const uint32_t eq_before = block_excl_scan(is_eq ? 1u : 0u, sh, eq_total);
-    const bool take = is_gt || (is_eq && eqb + eq_before < need);
-    uint32_t sel_total;
-    const uint32_t sel_before = block_excl_scan(take ? 1u : 0u, sh, sel_total);
-    if (take && off + sel_before < (uint32_t)K) out[off + sel_before] = i;  // bound: never past K
-    off += sel_total;
-    eqb += eq_total;
+  const int i1 = min((int)(blockIdx.x + 1) * kSlice, C);
+  const int first = blockIdx.x * kSlice + threadIdx.x * kPer;
+  const int cnt = max(0, min(kPer, i1 - first));  // valid candidates of this thread
+  uint32_t u[kPer];
+#pragma unroll
+  for (int r = 0; r < kPer; ++r) u[r] = r < cnt ? __float_as_uint(s[first + r]) : 0u;
+  uint32_t neq = 0;
+#pragma unroll
+  for (int r = 0; r < kPer; ++r) neq += (r < cnt && u[r] == T) ? 1u : 0u;
+  uint32_t total;
+  uint32_t eqr = eqb + block_excl_scan(neq, sh, total);  // equal candidates before this thread
+  uint32_t take = 0, ntake = 0;
+#pragma unroll
+  for (int r = 0; r < kPer; ++r) {
+    const bool valid = r < cnt;
+    const bool is_eq = valid && u[r] == T;
+    const bool t = (valid && u[r] > T) || (is_eq && eqr < need);
+    eqr += is_eq ? 1u : 0u;
+    take |= (t ? 1u : 0u) << r;
+    ntake += t ? 1u : 0u;
+  }
+  uint32_t o = off + block_excl_scan(ntake, sh, total);
+#pragma unroll
+  for (int r = 0; r < kPer; ++r) {
+    if ((take >> r) & 1u) {
+      if (o < (uint32_t)K) out[o] = first + r;  // bound: never past K
+      ++o;
+    }
   }
 }
 

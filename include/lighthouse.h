@@ -135,7 +135,9 @@ lh_status lh_topk(const lh_shape *shape, const float *score, int32_t *sel, void 
  * level) ascending with end(l,j) = (j+1)*p^l - 1.  Writes sub_idx [B,H,S]
  * (flat index per position), pos [B,H,M] (position per entry, -1 if not
  * selected) and copies the rows of q/k/v (level 0) or pq/pk/pv (levels >= 1)
- * into qs,ks,vs [B,H,S,d].  ws: ws_gather bytes (may be 0). */
+ * into qs,ks,vs [B,H,S,d].  sel must be strictly ascending within [0, C), as
+ * lh_topk writes it; for any other sel the outputs are unspecified, but no
+ * write leaves sub_idx, pos, qs, ks, vs.  ws: ws_gather bytes (may be 0). */
 lh_status lh_gather(const lh_shape *shape, const int32_t *sel, const void *q, const void *k,
                     const void *v, const void *pq, const void *pk, const void *pv,
                     int32_t *sub_idx, int32_t *pos, void *qs, void *ks, void *vs, void *ws,

@@ -95,8 +95,9 @@ def run_case(case):
     lb.lh_score(shape, q, k, r["score"], lb.workspace(z.ws_score))
     r["sel"] = e(B, H, z.K, dtype=torch.int32)
     lb.lh_topk(shape, f32(o("score")), r["sel"], lb.workspace(z.ws_topk))
-    r["sub_idx"] = e(B, H, S, dtype=torch.int32)
-    r["pos"] = e(B, H, z.M, dtype=torch.int32)
+    # sentinel-filled: every slot the gather must write is checked, not inherited
+    r["sub_idx"] = torch.full((B, H, S), 0x5A5A5A5A, dtype=torch.int32, device="cuda")
+    r["pos"] = torch.full((B, H, z.M), 0x5A5A5A5A, dtype=torch.int32, device="cuda")
     r["qs"], r["ks"], r["vs"] = (e(B, H, S, d) for _ in range(3))
     opyr = {n: to_device(pyr[n], dt) for n in pyr}
     lb.lh_gather(shape, i32(o("sel")) if z.K else None, q, k, v, opyr["pq"], opyr["pk"],
