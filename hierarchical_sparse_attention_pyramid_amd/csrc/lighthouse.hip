@@ -41,10 +41,14 @@ struct Plan {
   size_t sums_rows[2];  // rows per head of the A / B f32 sum buffers
 };
 
+#ifndef LH_POOL_TOKCHUNK
+#define LH_POOL_TOKCHUNK 64
+#endif
+
 int lam_max(int p) {
   int lam = 1;
   int64_t pw = p;
-  while (lam < lh::kStageLevels && pw * p <= 64) {
+  while (lam < lh::kStageLevels && pw * p <= LH_POOL_TOKCHUNK) {
     pw *= p;
     ++lam;
   }
@@ -120,7 +124,7 @@ lh_status make_plan(const lh_shape* s, Plan& P) {
       for (int i = 0; i < lam; ++i) plam *= s->p;
       // token passes walk 64-row chunks; upper passes see p^lvl times fewer
       // rows, so they take one span per row group to keep the GPU busy
-      const int64_t rep = lvl == 0 ? std::max<int64_t>(1, 64 / plam) : 1;
+      const int64_t rep = lvl == 0 ? std::max<int64_t>(1, LH_POOL_TOKCHUNK / plam) : 1;
       const int64_t rows_in = s->N / g.pw[lvl];
       Stage t{lvl, lam, (int)(plam * rep), rows_in, rows_in / plam, -1};
       P.st[P.nstages++] = t;

@@ -275,15 +275,16 @@ __global__ __launch_bounds__(256) void pool_bwd_kernel(PoolBwdArgs a) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[l][e] = 0.f;
   }
-  // c_t on the token pass.  p a power of two >= 4: the row group is 64
-  // aligned rows, so levels with p^l >= 64 give the same count to all of its
-  // rows (counted once here) and at most two inner levels vary per row.
-  // Other p: the ancestor walk of counts.
-  const bool fastc = FIRST && g.log2p >= 2;
+  // c_t on the token pass.  p a power of two >= 4 and a chunk of 2^lc
+  // aligned rows with 3 log2(p) >= lc: levels with p^l >= 2^lc give the same
+  // count to all rows of the chunk (counted once here) and at most two inner
+  // levels vary per row.  Otherwise: the ancestor walk of counts.
+  const int lc = 31 - __builtin_clz((unsigned)a.chunk);
+  const bool fastc = FIRST && g.log2p >= 2 && (1 << lc) == a.chunk && 3 * g.log2p >= lc;
   int cnt_outer = 0;
   if (fastc) {
     for (int l = 1; l < g.L; ++l)
-      if (g.log2p * l >= 6) cnt_outer += posf(l, (int32_t)(r0 >> (g.log2p * l))) >= 0;
+      if (g.log2p * l >= lc) cnt_outer += posf(l, (int32_t)(r0 >> (g.log2p * l))) >= 0;
   }
   AncestorWalk<0, 1> walk;
   for (int rb = 0; rb < nrows; rb += kRowsInFlight) {
@@ -305,7 +306,7 @@ __global__ __launch_bounds__(256) void pool_bwd_kernel(PoolBwdArgs a) {
           ct += cnt_outer;
 #pragma unroll
           for (int l = 1; l <= 2; ++l)
-            if (l < g.L && g.log2p * l < 6) ct += posf(l, (int32_t)(row >> (g.log2p * l))) >= 0;
+            if (l < g.L && g.log2p * l < lc) ct += posf(l, (int32_t)(row >> (g.log2p * l))) >= 0;
         } else {
           walk.advance((int32_t)row, posf, nullptr, g, true, lane);
           ct += walk.cnt[1];
