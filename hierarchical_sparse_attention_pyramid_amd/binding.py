@@ -29,7 +29,8 @@ class LighthouseError(RuntimeError):
 class Shape(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int64), ("H", ctypes.c_int64), ("N", ctypes.c_int64),
                 ("d", ctypes.c_int64), ("p", ctypes.c_int32), ("L", ctypes.c_int32),
-                ("S", ctypes.c_int64), ("dtype", ctypes.c_int32)]
+                ("S", ctypes.c_int64), ("dtype", ctypes.c_int32),
+                ("qkv_stride", ctypes.c_int64 * 3), ("out_stride", ctypes.c_int64 * 3)]
 
 
 class Sizes(ctypes.Structure):
@@ -117,10 +118,35 @@ def _check(status: int):
         raise LighthouseError(status, load_library().lh_last_error().decode())
 
 
-def make_shape(B, H, N, d, p, L, S, dtype) -> Shape:
+def make_shape(B, H, N, d, p, L, S, dtype, qkv_stride=None, out_stride=None) -> Shape:
+    """Shape with optional element strides (b, h, n) of the token tensors:
+    qkv_stride for q, k, v, dq, dk, dv; out_stride for out and dout (None =
+    packed [B,H,N,d])."""
     if isinstance(dtype, torch.dtype):
         dtype = DTYPES[dtype]
-    return Shape(B, H, N, d, p, L, S, dtype)
+    sh = Shape(B, H, N, d, p, L, S, dtype)
+    if qkv_stride is not None:
+        sh.qkv_stride = (ctypes.c_int64 * 3)(*qkv_stride)
+    if out_stride is not None:
+        sh.out_stride = (ctypes.c_int64 * 3)(*out_stride)
+    return sh
+
+
+def token_strides(*ts):
+    """Common (b, h, n) element strides of [B,H,N,d] views whose last
+    dimension is contiguous, or None if they differ or do not qualify."""
+    if any(t.dim() != 4 or t.stride(3) != 1 for t in ts):
+        return None
+    # the stride of an extent-1 dimension is never used (and may be anything)
+    st = {tuple(0 if t.shape[i] == 1 else t.stride(i) for i in range(3)) for t in ts}
+    return st.pop() if len(st) == 1 else None
+
+
+def with_strides(shape: Shape, qkv_stride=None, out_stride=None) -> Shape:
+    """A copy of `shape` with the given token strides (None = keep)."""
+    return make_shape(shape.B, shape.H, shape.N, shape.d, shape.p, shape.L, shape.S, shape.dtype,
+                      tuple(shape.qkv_stride) if qkv_stride is None else qkv_stride,
+                      tuple(shape.out_stride) if out_stride is None else out_stride)
 
 
 # ------------------------------------------------------------- the C ABI
@@ -238,19 +264,44 @@ def workspace(nbytes: int, device="cuda") -> torch.Tensor | None:
     return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device) if nbytes else None
 
 
-def forward(q, k, v, p: int, L: int, S: int, stream=None):
-    """out, buffers, shape for [B,H,N,d] device tensors (fp32 or bf16)."""
+def forward(q, k, v, p: int, L: int, S: int, out=None, stream=None):
+    """out, buffers, shape for [B,H,N,d] device tensors (fp32 or bf16).
+
+    q, k, v may be strided views sharing one layout (last dimension
+    contiguous), e.g. slices of a packed projection; otherwise they are made
+    contiguous.  `out`, if given, is a [B,H,N,d] view to write into (any
+    layout with a contiguous last dimension); else a packed tensor is
+    allocated."""
     B, H, N, d = q.shape
-    shape = make_shape(B, H, N, d, p, L, S, q.dtype)
+    st = token_strides(q, k, v)
+    if st is None:
+        q, k, v = (t.contiguous() for t in (q, k, v))
+        st = token_strides(q, k, v)
+    if out is None:
+        out = torch.empty(B, H, N, d, dtype=q.dtype, device=q.device)
+    ost = token_strides(out)
+    if ost is None:
+        raise ValueError("out must be a [B,H,N,d] view with a contiguous last dimension")
+    shape = make_shape(B, H, N, d, p, L, S, q.dtype, st, ost)
     bufs = LayerBuffers(shape, q.device)
-    out = torch.empty_like(q)
     ws = workspace(bufs.sizes.ws_forward, q.device)
     lh_forward(shape, q, k, v, out, bufs, ws, stream)
     return out, bufs, shape
 
 
-def backward(shape, dout, bufs: LayerBuffers, stream=None):
-    dq, dk, dv = (torch.empty_like(dout) for _ in range(3))
+def backward(shape, dout, bufs: LayerBuffers, dq=None, dk=None, dv=None, stream=None):
+    """dq, dk, dv of the forward that filled `bufs`.  dout: any [B,H,N,d]
+    layout with a contiguous last dimension (else made contiguous); dq, dk,
+    dv: views sharing one layout to write into, or None for packed tensors."""
+    if token_strides(dout) is None:
+        dout = dout.contiguous()
+    if dq is None:
+        dq, dk, dv = (torch.empty(shape.B, shape.H, shape.N, shape.d, dtype=dout.dtype,
+                                  device=dout.device) for _ in range(3))
+    gst = token_strides(dq, dk, dv)
+    if gst is None:
+        raise ValueError("dq, dk, dv must be [B,H,N,d] views sharing one layout")
+    call_shape = with_strides(shape, gst, token_strides(dout))
     ws = workspace(bufs.sizes.ws_backward, dout.device)
-    lh_backward(shape, dout, bufs, dq, dk, dv, ws, stream)
+    lh_backward(call_shape, dout, bufs, dq, dk, dv, ws, stream)
     return dq, dk, dv

@@ -24,6 +24,22 @@ struct Geo {
   float inv_pw[kMaxLevels];      // 1 / p^l rounded to float (exact when p is a power of two)
 };
 
+// Element strides of a [B, H, rows, d] tensor whose rows are d contiguous
+// elements: row r of head bh = b*H + h starts at element b*sb + h*sh + r*sn.
+struct Lay {
+  int64_t sb, sh, sn;
+  int32_t H;
+  __host__ __device__ __forceinline__ int64_t head(int64_t bh) const {
+    const int64_t b = bh / H;
+    return b * sb + (bh - b * H) * sh;
+  }
+};
+
+// The packed layout [B][H][rows][d].
+__host__ __device__ inline Lay packed_lay(int64_t H, int64_t rows, int64_t d) {
+  return Lay{H * rows * d, rows * d, d, (int32_t)H};
+}
+
 __device__ __forceinline__ int32_t div_pw(int32_t t, const Geo& g, int l) {
   return g.log2p >= 0 ? (t >> (g.log2p * l)) : t / g.pw[l];
 }

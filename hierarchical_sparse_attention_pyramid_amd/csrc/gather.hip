@@ -80,7 +80,7 @@ struct Ranker {
 
 template <typename T>
 __global__ __launch_bounds__(kThreads) void gather_kernel(
-    const int32_t* sel, const void* q, const void* k, const void* v, const void* pq,
+    const int32_t* sel, const void* q, const void* k, const void* v, Lay lq, const void* pq,
     const void* pk, const void* pv, int32_t* sub_idx, int32_t* pos, void* qs, void* ks, void* vs,
     Geo g, int32_t stride, int32_t ns) {
   __shared__ int32_t samp[kMaxSamples];
@@ -139,8 +139,9 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(
   auto src_of = [&](int e, int t) -> const f32x4* {
     const int32_t l = s_l[e];
     const void* base = l == 0 ? (t == 0 ? q : (t == 1 ? k : v)) : (t == 0 ? pq : (t == 1 ? pk : pv));
-    const int64_t row = l == 0 ? bh * g.N + s_j[e] : bh * (int64_t)(g.M - g.N) + (s_f[e] - g.N);
-    return reinterpret_cast<const f32x4*>(static_cast<const char*>(base) + row * g.d * es);
+    const int64_t el = l == 0 ? lq.head(bh) + s_j[e] * lq.sn
+                              : (bh * (int64_t)(g.M - g.N) + (s_f[e] - g.N)) * g.d;
+    return reinterpret_cast<const f32x4*>(static_cast<const char*>(base) + el * es);
   };
   auto dst_of = [&](int t, int32_t p) -> f32x4* {
     void* base = t == 0 ? qs : (t == 1 ? ks : vs);
@@ -240,9 +241,9 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(
 
 }  // namespace
 
-hipError_t launch_gather(const int32_t* sel, const void* const qkv[3], const void* const pyr[3],
-                         int32_t* sub_idx, int32_t* pos, void* const sub[3], const Geo& g,
-                         int dtype, int64_t BH, hipStream_t st) {
+hipError_t launch_gather(const int32_t* sel, const void* const qkv[3], const Lay& lq,
+                         const void* const pyr[3], int32_t* sub_idx, int32_t* pos,
+                         void* const sub[3], const Geo& g, int dtype, int64_t BH, hipStream_t st) {
   if (g.S == 0) return hipSuccess;
   // sample stride: at least 64, and at most kMaxSamples samples
   const int64_t K = g.K;
@@ -250,11 +251,11 @@ hipError_t launch_gather(const int32_t* sel, const void* const qkv[3], const voi
   const int32_t ns = (int32_t)((K + stride - 1) / stride);
   const dim3 grid((unsigned)((g.S + kEntries - 1) / kEntries), (unsigned)BH);
   if (dtype == 1)
-    gather_kernel<__bf16><<<grid, kThreads, 0, st>>>(sel, qkv[0], qkv[1], qkv[2], pyr[0], pyr[1],
+    gather_kernel<__bf16><<<grid, kThreads, 0, st>>>(sel, qkv[0], qkv[1], qkv[2], lq, pyr[0], pyr[1],
                                                      pyr[2], sub_idx, pos, sub[0], sub[1], sub[2],
                                                      g, (int32_t)stride, ns);
   else
-    gather_kernel<float><<<grid, kThreads, 0, st>>>(sel, qkv[0], qkv[1], qkv[2], pyr[0], pyr[1],
+    gather_kernel<float><<<grid, kThreads, 0, st>>>(sel, qkv[0], qkv[1], qkv[2], lq, pyr[0], pyr[1],
                                                     pyr[2], sub_idx, pos, sub[0], sub[1], sub[2],
                                                     g, (int32_t)stride, ns);
   return hipGetLastError();

@@ -13,7 +13,8 @@ namespace lh {
 constexpr int kStageLevels = 3;
 
 struct PoolFwdArgs {
-  const void* in[3];     // stage input: tokens [BH][N][d] (dtype) or f32 sums [BH][in_rows][d]
+  const void* in[3];     // stage input: tokens (dtype, layout lin) or f32 sums [BH][in_rows][d]
+  Lay lin;               // row layout of `in`
   void* pyr[3];          // pyramid rows [BH][M-N][d] (dtype); null = do not pool
   float* sums_out[3];    // f32 sums of this stage's top level [BH][out_rows][d], or null
   float* score;          // [BH][M] or null
@@ -26,7 +27,8 @@ struct PoolFwdArgs {
 };
 
 struct PoolBwdArgs {
-  const void* in;        // dout [BH][N][d] (dtype) or f32 sums [BH][in_rows][d]
+  const void* in;        // dout (dtype, layout lin) or f32 sums [BH][in_rows][d]
+  Lay lin;               // row layout of `in`
   void* dos;             // [BH][S][d] (dtype)
   float* sums_out;       // [BH][out_rows][d] or null
   const int32_t* pos;    // [BH][M]
@@ -37,7 +39,8 @@ struct PoolBwdArgs {
 
 struct BcastArgs {
   const float* src[3];   // [BH][S][d] float32
-  void* out[3];          // [BH][N][d]
+  void* out[3];          // [B,H,N,d] token tensors, layout lout
+  Lay lout;
   const int32_t* pos;    // [BH][M]
   int32_t mean;          // 1: mean over contributors; 0: weight 1/p^level
   Geo g;
@@ -56,9 +59,10 @@ hipError_t launch_topk(const float* score, int32_t* sel, void* ws, const Geo& g,
                        hipStream_t st);
 
 // gather
-hipError_t launch_gather(const int32_t* sel, const void* const q[3], const void* const pyr[3],
-                         int32_t* sub_idx, int32_t* pos, void* const qs[3], const Geo& g,
-                         int dtype, int64_t BH, hipStream_t st);
+// q, k, v: token tensors of layout lq
+hipError_t launch_gather(const int32_t* sel, const void* const q[3], const Lay& lq,
+                         const void* const pyr[3], int32_t* sub_idx, int32_t* pos,
+                         void* const qs[3], const Geo& g, int dtype, int64_t BH, hipStream_t st);
 
 // attention
 hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, float* o, float* lse,

@@ -32,6 +32,7 @@ struct Stage {
 
 struct Plan {
   lh::Geo g;
+  lh::Lay tin, tout;  // token tensors: q, k, v, dq, dk, dv / out, dout
   int64_t B, H, BH;
   int dtype;
   size_t es;
@@ -53,6 +54,40 @@ int lam_max(int p) {
     ++lam;
   }
   return lam;
+}
+
+// Layout of the token tensors from optional element strides (all zero: the
+// packed [B,H,N,d] layout).  Rows must start on 16-byte boundaries and no two
+// elements of different (b, h, n) may share an address; the stride of a
+// dimension of extent 1 is ignored.
+lh_status token_layout(const lh_shape* s, const int64_t (&st)[3], const char* what,
+                       lh::Lay& out) {
+  if (st[0] == 0 && st[1] == 0 && st[2] == 0) {
+    out = lh::packed_lay(s->H, s->N, s->d);
+    return LH_OK;
+  }
+  const int64_t es = s->dtype == LH_BF16 ? 2 : 4;
+  const int64_t ext[3] = {s->B, s->H, s->N};
+  int order[3] = {0, 1, 2};
+  for (int i = 0; i < 3; ++i) {
+    if (ext[i] == 1) continue;  // index always 0: the stride is never used
+    if (st[i] < 1 || st[i] > (int64_t(1) << 40))
+      return fail(LH_EINVAL, std::string(what) + " strides must be positive (or all zero)");
+    if ((st[i] * es) % 16)
+      return fail(LH_EINVAL, std::string(what) + " strides must be multiples of 16 bytes");
+  }
+  std::sort(order, order + 3, [&](int a, int b) { return st[a] < st[b]; });
+  int64_t span = s->d;  // elements covered by the smaller dimensions
+  for (int k = 0; k < 3; ++k) {
+    const int i = order[k];
+    if (ext[i] == 1) continue;
+    if (st[i] < span)
+      return fail(LH_EINVAL, std::string(what) + " strides make rows overlap");
+    span = st[i] * (ext[i] - 1) + span;
+  }
+  out = lh::Lay{ext[0] == 1 ? 0 : st[0], ext[1] == 1 ? 0 : st[1], ext[2] == 1 ? 0 : st[2],
+                (int32_t)s->H};
+  return LH_OK;
 }
 
 lh_status make_plan(const lh_shape* s, Plan& P) {
@@ -92,6 +127,10 @@ lh_status make_plan(const lh_shape* s, Plan& P) {
     return fail(LH_EUNSUPPORTED, "B*H*M must stay below 2^31");
   if (s->S < nc || s->S > M)
     return fail(LH_EINVAL, "S must satisfy N/p^(L-1) <= S <= M (number of pyramid entries)");
+  if (s->H >= (int64_t(1) << 31)) return fail(LH_EUNSUPPORTED, "H must stay below 2^31");
+  lh_status ls;
+  if ((ls = token_layout(s, s->qkv_stride, "qkv", P.tin)) != LH_OK) return ls;
+  if ((ls = token_layout(s, s->out_stride, "out", P.tout)) != LH_OK) return ls;
   g.N = (int32_t)s->N;
   g.d = (int32_t)s->d;
   g.p = s->p;
@@ -185,6 +224,13 @@ lh_status check_ws(void* ws, size_t have, size_t need) {
 #define LH_NEED(ptr, name) \
   if (!(ptr)) return fail(LH_EINVAL, name " is null")
 
+// Token tensors: non-null and 16-byte aligned (rows are moved in 16-byte
+// vectors).
+#define LH_TOK(ptr, name)                                                \
+  if (!(ptr)) return fail(LH_EINVAL, name " is null");                   \
+  if (reinterpret_cast<uintptr_t>(ptr) % 16)                             \
+  return fail(LH_EINVAL, name " must be 16-byte aligned")
+
 #define LH_HIP(call, where)                       \
   do {                                            \
     const hipError_t e_ = (call);                 \
@@ -206,6 +252,7 @@ lh_status run_pool(const Plan& P, const void* q, const void* k, const void* v, v
       a.sums_out[i] = (do_pool && t.out_buf >= 0) ? sums_ptr(P, ws, t.out_buf, i) : nullptr;
     }
     a.score = do_score ? score : nullptr;
+    a.lin = s == 0 ? P.tin : lh::packed_lay(P.H, t.rows_in, P.g.d);
     a.in_rows = t.rows_in;
     a.out_rows = t.rows_out;
     a.lvl0 = t.lvl0;
@@ -237,9 +284,9 @@ lh_status lh_build_pyramid(const lh_shape* shape, const void* q, const void* k, 
   Plan P;
   lh_status s = make_plan(shape, P);
   if (s != LH_OK) return s;
-  LH_NEED(q, "q");
-  LH_NEED(k, "k");
-  LH_NEED(v, "v");
+  LH_TOK(q, "q");
+  LH_TOK(k, "k");
+  LH_TOK(v, "v");
   if (P.sz.bytes_pyramid) {
     LH_NEED(pq, "pq");
     LH_NEED(pk, "pk");
@@ -256,8 +303,8 @@ lh_status lh_score(const lh_shape* shape, const void* q, const void* k, float* s
   Plan P;
   lh_status s = make_plan(shape, P);
   if (s != LH_OK) return s;
-  LH_NEED(q, "q");
-  LH_NEED(k, "k");
+  LH_TOK(q, "q");
+  LH_TOK(k, "k");
   LH_NEED(score, "score");
   (void)ws;
   (void)ws_bytes;
@@ -288,9 +335,9 @@ lh_status lh_gather(const lh_shape* shape, const int32_t* sel, const void* q, co
   (void)ws;
   (void)ws_bytes;
   if (P.g.K > 0) LH_NEED(sel, "sel");
-  LH_NEED(q, "q");
-  LH_NEED(k, "k");
-  LH_NEED(v, "v");
+  LH_TOK(q, "q");
+  LH_TOK(k, "k");
+  LH_TOK(v, "v");
   if (P.sz.bytes_pyramid) {
     LH_NEED(pq, "pq");
     LH_NEED(pk, "pk");
@@ -304,7 +351,7 @@ lh_status lh_gather(const lh_shape* shape, const int32_t* sel, const void* q, co
   const void* lv0[3] = {q, k, v};
   const void* pyr[3] = {pq, pk, pv};
   void* sub[3] = {qs, ks, vs};
-  LH_HIP(lh::launch_gather(sel, lv0, pyr, sub_idx, pos, sub, P.g, P.dtype, P.BH,
+  LH_HIP(lh::launch_gather(sel, lv0, P.tin, pyr, sub_idx, pos, sub, P.g, P.dtype, P.BH,
                            static_cast<hipStream_t>(stream)),
          "gather");
   return LH_OK;
@@ -333,12 +380,13 @@ lh_status lh_scatter(const lh_shape* shape, const float* os, const int32_t* pos,
   if (s != LH_OK) return s;
   LH_NEED(os, "os");
   LH_NEED(pos, "pos");
-  LH_NEED(out, "out");
+  LH_TOK(out, "out");
   lh::BcastArgs a{};
   a.src[0] = os;
   a.out[0] = out;
   a.pos = pos;
   a.mean = 1;
+  a.lout = P.tout;
   a.g = P.g;
   LH_HIP(lh::launch_bcast(a, P.dtype, 1, P.BH, static_cast<hipStream_t>(stream)),
          "scatter");
@@ -348,10 +396,10 @@ lh_status lh_scatter(const lh_shape* shape, const float* os, const int32_t* pos,
 static lh_status check_forward_args(const Plan& P, const void* q, const void* k, const void* v,
                                     void* out, const lh_buffers* b) {
   LH_NEED(b, "buffers");
-  LH_NEED(q, "q");
-  LH_NEED(k, "k");
-  LH_NEED(v, "v");
-  LH_NEED(out, "out");
+  LH_TOK(q, "q");
+  LH_TOK(k, "k");
+  LH_TOK(v, "v");
+  LH_TOK(out, "out");
   if (P.sz.bytes_pyramid) {
     LH_NEED(b->pq, "buffers.pq");
     LH_NEED(b->pk, "buffers.pk");
@@ -382,7 +430,7 @@ static lh_status run_forward(const Plan& P, const void* q, const void* k, const 
   const void* lv0[3] = {q, k, v};
   const void* pyr[3] = {b->pq, b->pk, b->pv};
   void* sub[3] = {b->qs, b->ks, b->vs};
-  LH_HIP(lh::launch_gather(b->sel, lv0, pyr, b->sub_idx, b->pos, sub, P.g, P.dtype, P.BH, st),
+  LH_HIP(lh::launch_gather(b->sel, lv0, P.tin, pyr, b->sub_idx, b->pos, sub, P.g, P.dtype, P.BH, st),
          "gather");
   if (ev) LH_HIP(hipEventRecord(ev[2], st), "event");
   LH_HIP(lh::launch_attn_fwd(b->qs, b->ks, b->vs, b->os, b->lse, P.g.S, P.g.d, P.dtype, P.BH, st),
@@ -393,6 +441,7 @@ static lh_status run_forward(const Plan& P, const void* q, const void* k, const 
   a.out[0] = out;
   a.pos = b->pos;
   a.mean = 1;
+  a.lout = P.tout;
   a.g = P.g;
   LH_HIP(lh::launch_bcast(a, P.dtype, 1, P.BH, st), "scatter");
   if (ev) LH_HIP(hipEventRecord(ev[4], st), "event");
@@ -418,6 +467,7 @@ static lh_status run_scatter_bwd(const Plan& P, const void* dout, const int32_t*
     a.dos = dos;
     a.sums_out = t.out_buf >= 0 ? sums_ptr(P, ws, t.out_buf, 0) : nullptr;
     a.pos = pos;
+    a.lin = s == 0 ? P.tout : lh::packed_lay(P.H, t.rows_in, P.g.d);
     a.in_rows = t.rows_in;
     a.out_rows = t.rows_out;
     a.lvl0 = t.lvl0;
@@ -434,7 +484,7 @@ lh_status lh_scatter_backward(const lh_shape* shape, const void* dout, const int
   Plan P;
   lh_status s = make_plan(shape, P);
   if (s != LH_OK) return s;
-  LH_NEED(dout, "dout");
+  LH_TOK(dout, "dout");
   LH_NEED(pos, "pos");
   LH_NEED(dos, "dos");
   if ((s = check_ws(ws, ws_bytes, P.sz.ws_scatter_backward)) != LH_OK) return s;
@@ -476,9 +526,9 @@ lh_status lh_gather_backward(const lh_shape* shape, const float* dqs, const floa
   LH_NEED(dks, "dks");
   LH_NEED(dvs, "dvs");
   LH_NEED(pos, "pos");
-  LH_NEED(dq, "dq");
-  LH_NEED(dk, "dk");
-  LH_NEED(dv, "dv");
+  LH_TOK(dq, "dq");
+  LH_TOK(dk, "dk");
+  LH_TOK(dv, "dv");
   lh::BcastArgs a{};
   a.src[0] = dqs;
   a.src[1] = dks;
@@ -488,6 +538,7 @@ lh_status lh_gather_backward(const lh_shape* shape, const float* dqs, const floa
   a.out[2] = dv;
   a.pos = pos;
   a.mean = 0;
+  a.lout = P.tin;
   a.g = P.g;
   LH_HIP(lh::launch_bcast(a, P.dtype, 3, P.BH, static_cast<hipStream_t>(stream)),
          "gather_backward");
@@ -497,16 +548,16 @@ lh_status lh_gather_backward(const lh_shape* shape, const float* dqs, const floa
 static lh_status check_backward_args(const void* dout, const lh_buffers* b, void* dq, void* dk,
                                      void* dv) {
   LH_NEED(b, "buffers");
-  LH_NEED(dout, "dout");
+  LH_TOK(dout, "dout");
   LH_NEED(b->pos, "buffers.pos");
   LH_NEED(b->qs, "buffers.qs");
   LH_NEED(b->ks, "buffers.ks");
   LH_NEED(b->vs, "buffers.vs");
   LH_NEED(b->os, "buffers.os");
   LH_NEED(b->lse, "buffers.lse");
-  LH_NEED(dq, "dq");
-  LH_NEED(dk, "dk");
-  LH_NEED(dv, "dv");
+  LH_TOK(dq, "dq");
+  LH_TOK(dk, "dk");
+  LH_TOK(dv, "dv");
   return LH_OK;
 }
 
@@ -541,6 +592,7 @@ static lh_status run_backward(const Plan& P, const void* dout, const lh_buffers*
   a.out[2] = dv;
   a.pos = b->pos;
   a.mean = 0;
+  a.lout = P.tin;
   a.g = P.g;
   LH_HIP(lh::launch_bcast(a, P.dtype, 3, P.BH, st), "gather_backward");
   if (ev) LH_HIP(hipEventRecord(ev[4], st), "event");

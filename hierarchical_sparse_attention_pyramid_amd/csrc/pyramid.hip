@@ -84,7 +84,7 @@ __device__ __forceinline__ void pool_pass(const PoolFwdArgs& a, const int (&tid)
   float* so[NT];
 #pragma unroll
   for (int i = 0; i < NT; ++i) {
-    in[i] = a.in[tid[i]] ? static_cast<const Tin*>(a.in[tid[i]]) + bh * a.in_rows * d + 8 * lane
+    in[i] = a.in[tid[i]] ? static_cast<const Tin*>(a.in[tid[i]]) + a.lin.head(bh) + 8 * lane
                          : nullptr;  // score-only passes above level 0 read no rows
     pyr[i] = do_pool ? static_cast<Tout*>(a.pyr[tid[i]]) + bh * (int64_t)(g.M - g.N) * d + 8 * lane
                      : nullptr;
@@ -113,7 +113,8 @@ __device__ __forceinline__ void pool_pass(const PoolFwdArgs& a, const int (&tid)
       for (int u = 0; u < kRowsInFlight; ++u) {
         const int64_t row = r0 + min(rb + u, nrows - 1);
 #pragma unroll
-        for (int i = 0; i < NT; ++i) Row8<Tin>::template load<kStream>(in[i] + row * d, xs[u][i]);
+        for (int i = 0; i < NT; ++i)
+          Row8<Tin>::template load<kStream>(in[i] + row * a.lin.sn, xs[u][i]);
       }
     }
     float sin[kRowsInFlight];
@@ -263,7 +264,7 @@ __global__ __launch_bounds__(256) void pool_bwd_kernel(PoolBwdArgs a) {
 
   const int64_t r0 = c * a.chunk;
   const int nrows = (int)min((int64_t)a.chunk, a.in_rows - r0);
-  const Tin* in = static_cast<const Tin*>(a.in) + bh * a.in_rows * d + 8 * lane;
+  const Tin* in = static_cast<const Tin*>(a.in) + a.lin.head(bh) + 8 * lane;
   Tout* dos = static_cast<Tout*>(a.dos) + bh * (int64_t)g.S * d + 8 * lane;
   float* so = a.sums_out ? a.sums_out + bh * a.out_rows * d + 8 * lane : nullptr;
 
@@ -293,7 +294,7 @@ __global__ __launch_bounds__(256) void pool_bwd_kernel(PoolBwdArgs a) {
 #pragma unroll
     for (int u = 0; u < kRowsInFlight; ++u) {
       const int64_t row = r0 + min(rb + u, nrows - 1);
-      Row8<Tin>::template load<kStream>(in + row * d, xs[u]);
+      Row8<Tin>::template load<kStream>(in + row * a.lin.sn, xs[u]);
       if constexpr (FIRST) pt[u] = sp[row - B0];
     }
 #pragma unroll

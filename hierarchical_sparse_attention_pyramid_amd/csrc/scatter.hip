@@ -72,7 +72,7 @@ __global__ __launch_bounds__(256) void bcast_kernel(BcastArgs a) {
 #pragma unroll
   for (int i = 0; i < NT; ++i) {
     src[i] = a.src[i] + bh * (int64_t)g.S * g.d;
-    out[i] = static_cast<Tout*>(a.out[i]) + bh * (int64_t)g.N * g.d + kE * lane;
+    out[i] = static_cast<Tout*>(a.out[i]) + a.lout.head(bh) + kE * lane;
   }
   const int32_t t0 = ((int32_t)blockIdx.x * rgs + rg) * kTokPerGroup;
   if (t0 >= g.N) return;  // no block-wide barrier in this kernel
@@ -103,7 +103,7 @@ __global__ __launch_bounds__(256) void bcast_kernel(BcastArgs a) {
         float o[kE];
 #pragma unroll
         for (int e = 0; e < kE; ++e) o[e] = (w.A[1][i][e] + v0[u][i][e]) * rc;
-        Out4<Tout>::store(out[i] + (int64_t)(t + u) * g.d, o);
+        Out4<Tout>::store(out[i] + (int64_t)(t + u) * a.lout.sn, o);
       }
     }
   }
@@ -169,7 +169,7 @@ __global__ __launch_bounds__(256) void bcast_fast(BcastArgs a) {
   const int32_t t1 = min(t0 + kFastTok, g.N);
 
   const float* src = a.src[z] + bh * (int64_t)g.S * g.d + kE * lane;
-  Tout* out = static_cast<Tout*>(a.out[z]) + bh * (int64_t)g.N * g.d + kE * lane;
+  Tout* out = static_cast<Tout*>(a.out[z]) + a.lout.head(bh) + kE * lane;
   const bool mean = a.mean != 0;
 
   // levels 1 .. lam-1 are inner (p^l < 64), lam .. L-1 outer
@@ -278,7 +278,7 @@ __global__ __launch_bounds__(256) void bcast_fast(BcastArgs a) {
       float o[kE];
 #pragma unroll
       for (int e = 0; e < kE; ++e) o[e] = (A[0][e] + b.r0[u][e]) * rc;
-      Out4<Tout>::store(out + (int64_t)t * g.d, o);
+      Out4<Tout>::store(out + (int64_t)t * a.lout.sn, o);
     }
   };
   if (nin == 0) {  // A[0] must be the outer sum

@@ -13,6 +13,13 @@ the projections are plain dense GEMMs (torch, i.e. hipBLASLt / rocBLAS).
 Projections are bias-free and head-major: columns h*d .. h*d+d-1 of the
 projected queries belong to head h (likewise keys, values, and the rows of
 the output projection's input).
+
+The block keeps activations token-major: one GEMM projects x to a packed
+[B*N, 3*H*d] buffer, the layer reads q, k, v as strided [B,H,N,d] views of
+it and writes its output token-major, and its backward writes dq, dk, dv
+into one packed gradient buffer.  No layout copies run on either side of
+the layer, the gradient of x is one GEMM over the packed gradient, and the
+weight gradients of the three input projections are one GEMM.
 """
 from __future__ import annotations
 
@@ -22,11 +29,12 @@ from . import binding
 
 
 class LighthouseFunction(torch.autograd.Function):
-    """out = Lighthouse(q, k, v) on [B, H, N, d] tensors; backward via lh_backward."""
+    """out = Lighthouse(q, k, v) on [B, H, N, d] tensors (strided views with a
+    contiguous last dimension and one common layout are used in place);
+    backward via lh_backward."""
 
     @staticmethod
     def forward(ctx, q, k, v, p: int, L: int, S: int):
-        q, k, v = (t.contiguous() for t in (q, k, v))
         out, bufs, shape = binding.forward(q, k, v, p, L, S)
         ctx.lh = (bufs, shape)
         return out
@@ -34,13 +42,42 @@ class LighthouseFunction(torch.autograd.Function):
     @staticmethod
     def backward(ctx, dout):
         bufs, shape = ctx.lh
-        dq, dk, dv = binding.backward(shape, dout.contiguous(), bufs)
+        dq, dk, dv = binding.backward(shape, dout, bufs)
         return dq, dk, dv, None, None, None
 
 
 def lighthouse(q, k, v, p: int, L: int, S: int):
     """Differentiable Lighthouse attention on [B, H, N, d] (fp32 or bf16)."""
     return LighthouseFunction.apply(q, k, v, p, L, S)
+
+
+def _heads(t2, B: int, N: int, H: int, d: int, part: int, parts: int):
+    """[B,H,N,d] view of columns part*H*d .. (part+1)*H*d of a [B*N, parts*H*d]
+    token-major buffer."""
+    return t2.view(B, N, parts, H, d)[:, :, part].permute(0, 2, 1, 3)
+
+
+class LighthousePackedFunction(torch.autograd.Function):
+    """o2 [B*N, H*d] = Lighthouse on the q, k, v column blocks of a packed
+    qkv2 [B*N, 3*H*d], both token-major; the gradient is one packed buffer."""
+
+    @staticmethod
+    def forward(ctx, qkv2, B: int, N: int, H: int, d: int, p: int, L: int, S: int):
+        qkv2 = qkv2.contiguous()
+        q, k, v = (_heads(qkv2, B, N, H, d, i, 3) for i in range(3))
+        o2 = torch.empty(B * N, H * d, dtype=qkv2.dtype, device=qkv2.device)
+        _, bufs, shape = binding.forward(q, k, v, p, L, S, out=_heads(o2, B, N, H, d, 0, 1))
+        ctx.lh = (bufs, shape, B, N, H, d)
+        return o2
+
+    @staticmethod
+    def backward(ctx, do2):
+        bufs, shape, B, N, H, d = ctx.lh
+        do2 = do2.contiguous()
+        dqkv2 = torch.empty(B * N, 3 * H * d, dtype=do2.dtype, device=do2.device)
+        binding.backward(shape, _heads(do2, B, N, H, d, 0, 1), bufs,
+                         *(_heads(dqkv2, B, N, H, d, i, 3) for i in range(3)))
+        return dqkv2, None, None, None, None, None, None, None
 
 
 class LighthouseAttention(torch.nn.Module):
@@ -61,15 +98,10 @@ class LighthouseAttention(torch.nn.Module):
         for w in (self.wq, self.wk, self.wv, self.wo):
             torch.nn.init.normal_(w, std=d_model ** -0.5)
 
-    def _heads(self, x2, w, B, N):
-        # [B*N, D] @ [D, H*d] -> [B, H, N, d] (2-D GEMM; heads made contiguous)
-        y = torch.nn.functional.linear(x2, w)
-        return y.view(B, N, self.H, self.d).transpose(1, 2).contiguous()
-
     def forward(self, x):
         B, N, D = x.shape
         x2 = x.reshape(B * N, D)
-        q, k, v = (self._heads(x2, w, B, N) for w in (self.wq, self.wk, self.wv))
-        o = lighthouse(q, k, v, self.p, self.L, self.S)
-        o2 = o.transpose(1, 2).reshape(B * N, self.H * self.d)
+        # one GEMM for the three input projections: [B*N, 3*H*d], token-major
+        qkv2 = torch.nn.functional.linear(x2, torch.cat((self.wq, self.wk, self.wv)))
+        o2 = LighthousePackedFunction.apply(qkv2, B, N, self.H, self.d, self.p, self.L, self.S)
         return torch.nn.functional.linear(o2, self.wo).view(B, N, D)

@@ -11,9 +11,11 @@
  *
  * Conventions shared by every entry point
  * ----------------------------------------
- *  - Tensors are caller-owned DEVICE memory, contiguous, row-major with the
- *    head dimension fastest.  The library never allocates device memory:
- *    scratch space comes from the `ws` argument, sized by lh_query_sizes().
+ *  - Tensors are caller-owned DEVICE memory, row-major with the head
+ *    dimension fastest, contiguous unless lh_shape gives strides for the
+ *    token tensors (see lh_shape).  The library never allocates device
+ *    memory: scratch space comes from the `ws` argument, sized by
+ *    lh_query_sizes().
  *  - Element type of q/k/v-like tensors is shape->dtype (LH_FP32: float,
  *    LH_BF16: bfloat16 bit patterns, 2 bytes).  Scores, lse and the
  *    subsequence gradients are float32; index tensors are int32.
@@ -61,12 +63,30 @@ typedef enum { LH_FP32 = 0, LH_BF16 = 1 } lh_dtype;
 
 /* Problem shape.  p = pooling factor, L = number of pyramid levels (level 0 =
  * tokens), S = subsequence length.  L = 1 means S = N and the layer is plain
- * dense causal attention. */
+ * dense causal attention.
+ *
+ * Token-tensor layouts (optional).  The [B,H,N,d] token tensors may be
+ * strided views, as a model's packed projections give them (e.g. q, k, v
+ * inside one [B, N, 3, H, d] buffer): element (b, h, n, i) sits at
+ * b*s[0] + h*s[1] + n*s[2] + i elements from the tensor's pointer.
+ *   qkv_stride: q, k, v (lh_build_pyramid, lh_score, lh_gather, lh_forward)
+ *               and the gradients dq, dk, dv (lh_gather_backward,
+ *               lh_backward);
+ *   out_stride: out (lh_scatter, lh_forward) and dout (lh_scatter_backward,
+ *               lh_backward).
+ * All three zero = the packed layout s = {H*N*d, N*d, d}.  Otherwise every
+ * stride of a dimension longer than 1 is positive and a multiple of 16
+ * bytes, and no two rows overlap (LH_EINVAL if not); the stride of a
+ * dimension of extent 1 is ignored.  Tensor pointers must be 16-byte aligned.  Every other
+ * tensor of the API (pyramid, scores, maps, subsequence tensors) is packed.
+ * Zero-initialising the struct keeps the packed layout. */
 typedef struct {
   int64_t B, H, N, d;
   int32_t p, L;
   int64_t S;
   int32_t dtype; /* lh_dtype */
+  int64_t qkv_stride[3];
+  int64_t out_stride[3];
 } lh_shape;
 
 /* Derived sizes (per (b,h) counts; byte sizes are for all B*H heads). */

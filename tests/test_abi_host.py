@@ -82,3 +82,39 @@ def test_null_pointers_and_small_workspace_are_rejected_without_a_gpu(lb):
     assert st == 3
     st = lib.lh_forward(ctypes.byref(shape), 1, 1, 1, 1, None, 1, z.ws_forward, None)
     assert st == 1 and b"buffers" in lib.lh_last_error()
+
+
+def _strided(lb, qkv=None, out=None, B=2, H=4, N=256, d=64, dtype=1):
+    return lb.make_shape(B, H, N, d, 4, 3, 40, dtype, qkv, out)
+
+
+@pytest.mark.parametrize("qkv,out,ok", [
+    ((256 * 3 * 4 * 64, 64, 3 * 4 * 64), None, True),           # q/k/v slices of a packed [B,N,3,H,d]
+    (None, (256 * 4 * 64, 64, 4 * 64), True),                   # token-major output [B,N,H,d]
+    ((4 * 256 * 64, 256 * 64, 64), (4 * 256 * 64, 256 * 64, 64), True),  # packed, given explicitly
+    ((256 * 4 * 64, 64, 64), None, False),                      # heads and tokens overlap
+    (None, (256 * 4 * 64, 64 * 256, 60), False),                # token rows overlap (60 < d)
+    ((256 * 4 * 68, 68, 4 * 68), None, False),                  # 136-byte head stride: not 16-byte multiple
+    ((0, 64, 4 * 64), None, False),                             # zero stride on a dimension of extent 2
+    ((4 * 256 * 64, 256 * 64, -64), None, False),               # negative stride
+])
+def test_token_strides_are_validated(lb, qkv, out, ok):
+    shape = _strided(lb, qkv, out)
+    if ok:
+        lb.lh_query_sizes(shape)
+    else:
+        with pytest.raises(lb.LighthouseError) as ei:
+            lb.lh_query_sizes(shape)
+        assert ei.value.status == 1 and b"strides" in lb.load_library().lh_last_error()
+
+
+def test_stride_of_an_extent_one_dimension_is_ignored(lb):
+    # B = 1: any batch stride, even one no row layout could use
+    lb.lh_query_sizes(_strided(lb, (3, 64, 4 * 64), None, B=1))
+
+
+def test_misaligned_token_pointer_is_rejected_without_a_gpu(lb):
+    lib = lb.load_library()
+    shape = lb.make_shape(1, 2, 256, 64, 4, 3, 40, 1)
+    st = lib.lh_score(ctypes.byref(shape), 4096 + 8, 4096, 4096, None, 0, None)
+    assert st == 1 and b"16-byte aligned" in lib.lh_last_error()
