@@ -3,7 +3,10 @@
 One step = lh_forward + lh_backward (every stage of the hot path) on one batch
 of synthetic input already resident in HBM.  The headline workload is the
 98,304-token training context (B=1, H=16, d=64, p=4, L=5, S=8192, bf16);
-`value` is its whole-job throughput in tokens/s.  Alongside:
+`value` is its whole-job throughput in tokens/s, with the step captured once
+in a HIP graph and replayed (the same kernels, launch for launch; a replay is
+checked bit for bit against the eager step first); the eagerly launched step
+time is reported beside it (config.eager_ms_per_step).  Alongside:
   * per-stage times from HIP events on the launch stream and each stage's
     fraction of its HBM or matrix-core roofline;
   * the 524,288-token layer (H=16, d=128, p=4, L=6, S=16384) forward and
@@ -170,6 +173,9 @@ class Layer:
         self.lb.lh_backward(self.shape, self.x["dout"], self.bufs, self.dq, self.dk, self.dv,
                             self.ws)
 
+    def outputs(self):
+        return (self.out, self.dq, self.dk, self.dv)
+
     def profile(self):
         x = self.x
         return self.lb.lh_profile_step(self.shape, x["q"], x["k"], x["v"], self.out, self.bufs,
@@ -187,6 +193,34 @@ def time_fn(torch, fn, steps, warmup):
     b.record()
     torch.cuda.synchronize()
     return a.elapsed_time(b) / steps
+
+
+def graph_time(torch, lay, steps, warmup):
+    """The forward+backward step captured once in a HIP graph and replayed:
+    ms per replay (warm-up, then exactly `steps` timed replays), after
+    checking that a replay reproduces the eager step's outputs bit for bit.
+    The captured work is the eager step's kernels, launch for launch."""
+    lay.step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in lay.outputs()]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        lay.step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        lay.step()
+    for t in lay.outputs():
+        t.zero_()
+    graph.replay()
+    torch.cuda.synchronize()
+    if not all(torch.equal(a, b) for a, b in zip(lay.outputs(), ref)):
+        raise RuntimeError("graph replay differs from the eager step")
+    ms = time_fn(torch, graph.replay, steps, warmup)
+    del graph
+    return ms
 
 
 def measured_ceilings(torch):
@@ -358,9 +392,11 @@ def main():
 
     cfg = synth.CONFIGS[HEADLINE]
     lay = Layer(cfg, torch, lb)
-    ms = time_fn(torch, lay.step, args.steps, args.warmup)
+    ms_eager = time_fn(torch, lay.step, args.steps, args.warmup)
+    ms = graph_time(torch, lay, args.steps, args.warmup)
     tokens = cfg.B * cfg.N
-    log(f"[bench] {cfg.name}: {ms:.3f} ms per forward+backward step")
+    log(f"[bench] {cfg.name}: {ms:.3f} ms per forward+backward step replayed from a HIP graph "
+        f"({ms_eager:.3f} ms launched eagerly)")
     ms_fwd = time_fn(torch, lay.forward, args.steps, 2)
     prof = [lay.profile() for _ in range(args.profile_reps)]
     stages_ms = {k: sorted(p[k] for p in prof)[len(prof) // 2] for k in prof[0]}
@@ -449,6 +485,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": cfg.name, "B": cfg.B, "H": cfg.H, "N": cfg.N, "d": cfg.d,
                    "p": cfg.p, "L": cfg.L, "S": cfg.S, "pass": "forward+backward",
+                   "launch": "hip_graph_replay", "eager_ms_per_step": round(ms_eager, 4),
                    "forward_only_ms": round(ms_fwd, 4)},
         "roofline": roof,
         "cpu_baseline": cpu,
