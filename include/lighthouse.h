@@ -36,6 +36,9 @@
  *    lh_last_error() gives a message for the calling thread.
  *  - Determinism: identical inputs give bit-identical outputs (no floating
  *    point atomics anywhere).
+ *  - Inputs are expected to be finite.  A NaN or infinity in q or k gives a
+ *    non-finite score, which the top-K ranks by its bit pattern (as a value
+ *    above every finite score); outputs touched by it are not meaningful.
  *  - Shape limits: 2 <= p <= 64, 1 <= L <= 16, N % p^(L-1) == 0,
  *    n_coarse <= S <= M, d in {64, 128}, B*H*M < 2^31 (p > 64 returns
  *    LH_EUNSUPPORTED: the pooling kernels stage a workgroup's positions in
