@@ -15,12 +15,12 @@
 // Both steps are exact integer work and give one deterministic answer.
 //
 // Workspace per head (uint32): [0] threshold prefix, [1] remaining count,
-// [2..3] unused, [4..4+2048) histogram, then four arrays of nblk block
-// counters (greater, equal, output offset, equal-before).  The serial steps
-// (bin pick, block-offset scan) are separate one-block-per-head launches: a
-// "last block finishes the pass" scheme would need a device-scope fence in
-// every block, which on a multi-XCD GPU (one L2 per XCD) costs more than a
-// launch.
+// [2..3] unused, [4..4+2048) histogram, then two arrays of nblk block
+// counters (candidates above and equal to the threshold).  The bin pick is
+// a separate one-block-per-head launch: a "last block finishes the pass"
+// scheme would need a device-scope fence in every block, which on a
+// multi-XCD GPU (one L2 per XCD) costs more than a launch.  Each block of the
+// compaction sums the counters of the blocks before it itself.
 #include "kernels.h"
 
 namespace lh {
@@ -32,7 +32,7 @@ constexpr int kSlice = 4096;  // candidates per block
 constexpr int kThreads = 256;
 
 __device__ __forceinline__ uint32_t* head_ws(void* ws, int64_t bh, int64_t nblk) {
-  return static_cast<uint32_t*>(ws) + bh * (4 + kBins + 4 * nblk);
+  return static_cast<uint32_t*>(ws) + bh * (4 + kBins + 2 * nblk);
 }
 
 __device__ __forceinline__ void pass_bits(int pass, int& shift, int& nbits) {
@@ -156,42 +156,13 @@ __global__ __launch_bounds__(kThreads) void topk_count(const float* score, void*
   }
 }
 
-// One block per head: output offset of every block (equal candidates are
-// taken in flat order until `need` of them are in).
-__global__ __launch_bounds__(kThreads) void topk_scan(void* ws, int64_t nblk) {
-  __shared__ uint32_t sh[kThreads / 64];
-  __shared__ uint32_t carry[2];
-  uint32_t* w = head_ws(ws, blockIdx.x, nblk);
-  uint32_t* blk = w + 4 + kBins;
-  const uint32_t need = w[1];
-  if (threadIdx.x == 0) carry[0] = carry[1] = 0;
-  __syncthreads();
-  for (int64_t b0 = 0; b0 < nblk; b0 += kThreads) {
-    const int64_t b = b0 + threadIdx.x;
-    const uint32_t g1 = b < nblk ? blk[b] : 0u;
-    const uint32_t e1 = b < nblk ? blk[nblk + b] : 0u;
-    uint32_t etot;
-    const uint32_t eqb = carry[1] + block_excl_scan(e1, sh, etot);
-    const uint32_t left = need > eqb ? need - eqb : 0u;
-    const uint32_t take = e1 < left ? e1 : left;
-    uint32_t otot;
-    const uint32_t off = carry[0] + block_excl_scan(g1 + take, sh, otot);
-    if (b < nblk) {
-      blk[2 * nblk + b] = off;
-      blk[3 * nblk + b] = eqb;
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      carry[0] += otot;
-      carry[1] += etot;
-    }
-    __syncthreads();
-  }
-}
-
 // Ordered compaction of one block's slice: thread t owns the contiguous
 // candidates i0 + 16t .. i0 + 16t + 15, so two block scans (equal-to-T ranks,
-// then output offsets) order the whole slice.
+// then output offsets) order the whole slice.  The slice's first output
+// position follows from the earlier slices' counts alone: every candidate
+// above T is taken, and candidates equal to T are taken in flat order until
+// `need` of them are in, so the earlier slices took GT + min(EQ, need) of
+// them (GT, EQ: their counts above and equal to T).
 __global__ __launch_bounds__(kThreads) void topk_write(const float* score, int32_t* sel, void* ws,
                                                        int64_t nblk, int32_t M, int32_t C,
                                                        int32_t K) {
@@ -201,8 +172,17 @@ __global__ __launch_bounds__(kThreads) void topk_write(const float* score, int32
   const uint32_t* w = head_ws(ws, bh, nblk);
   const uint32_t T = w[0], need = w[1];
   const uint32_t* blk = w + 4 + kBins;
-  const uint32_t off = blk[2 * nblk + blockIdx.x];
-  const uint32_t eqb = blk[3 * nblk + blockIdx.x];
+  uint32_t gt_part = 0, eq_part = 0;  // this thread's share of the earlier slices' counts
+  for (int64_t b = threadIdx.x; b < blockIdx.x; b += kThreads) {
+    gt_part += blk[b];
+    eq_part += blk[nblk + b];
+  }
+  uint32_t total;
+  block_excl_scan(gt_part, sh, total);
+  const uint32_t gt_before = total;
+  block_excl_scan(eq_part, sh, total);
+  const uint32_t eqb = total;  // candidates equal to T in the earlier slices
+  const uint32_t off = gt_before + (eqb < need ? eqb : need);
   const float* s = score + bh * M;
   int32_t* out = sel + bh * K;
   const int i1 = min((int)(blockIdx.x + 1) * kSlice, C);
@@ -214,7 +194,6 @@ __global__ __launch_bounds__(kThreads) void topk_write(const float* score, int32
   uint32_t neq = 0;
 #pragma unroll
   for (int r = 0; r < kPer; ++r) neq += (r < cnt && u[r] == T) ? 1u : 0u;
-  uint32_t total;
   uint32_t eqr = eqb + block_excl_scan(neq, sh, total);  // equal candidates before this thread
   uint32_t take = 0, ntake = 0;
 #pragma unroll
@@ -241,7 +220,7 @@ __global__ __launch_bounds__(kThreads) void topk_write(const float* score, int32
 int64_t topk_blocks(int64_t C) { return (C + kSlice - 1) / kSlice; }
 
 size_t topk_ws_bytes(int64_t BH, int64_t C) {
-  return (size_t)BH * (size_t)(4 + kBins + 4 * topk_blocks(C)) * sizeof(uint32_t);
+  return (size_t)BH * (size_t)(4 + kBins + 2 * topk_blocks(C)) * sizeof(uint32_t);
 }
 
 hipError_t launch_topk(const float* score, int32_t* sel, void* ws, const Geo& g, int64_t BH,
@@ -255,7 +234,6 @@ hipError_t launch_topk(const float* score, int32_t* sel, void* ws, const Geo& g,
     topk_pick<<<(unsigned)BH, kThreads, 0, st>>>(ws, nblk, pass);
   }
   topk_count<<<grid, kThreads, 0, st>>>(score, ws, nblk, g.M, g.C);
-  topk_scan<<<(unsigned)BH, kThreads, 0, st>>>(ws, nblk);
   topk_write<<<grid, kThreads, 0, st>>>(score, sel, ws, nblk, g.M, g.C, g.K);
   return hipGetLastError();
 }
