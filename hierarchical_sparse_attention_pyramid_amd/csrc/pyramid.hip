@@ -27,9 +27,6 @@ namespace {
 #ifndef LH_POOL_NT
 #define LH_POOL_NT 1
 #endif
-#ifndef LH_POOL_QKV1
-#define LH_POOL_QKV1 0
-#endif
 constexpr int kRowsInFlight = LH_POOL_ROWS;  // rows whose loads a row group issues together
 constexpr bool kStream = LH_POOL_NT != 0;    // token rows are read once: streaming loads
 
@@ -195,14 +192,9 @@ __global__ __launch_bounds__(256) void pool_fwd_kernel(PoolFwdArgs a, int do_poo
   const int64_t r0 = c * a.chunk;
   const int nrows = (int)min((int64_t)a.chunk, a.in_rows - r0);
   constexpr int kScore = FIRST ? 1 : 2;
-  // pass 1: q and k (with the scores); pass 2: v
+  // pass 1: q and k (with the scores); pass 2: v (two passes keep fewer
+  // rows' accumulators live in registers than one pass over all three)
   const int qk[2] = {0, 1};
-  if (LH_POOL_QKV1 && do_pool) {
-    const int qkv[3] = {0, 1, 2};
-    if (do_score) pool_pass<Tin, Tout, 3, kScore>(a, qkv, true, bh, r0, nrows, lane);
-    else pool_pass<Tin, Tout, 3, 0>(a, qkv, true, bh, r0, nrows, lane);
-    return;
-  }
   if (do_score) {
     pool_pass<Tin, Tout, 2, kScore>(a, qk, do_pool != 0, bh, r0, nrows, lane);
   } else if (do_pool) {
