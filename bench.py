@@ -18,7 +18,9 @@ time is reported beside it (config.eager_ms_per_step).  Alongside:
     peaks: a 1 GiB device copy (HBM) and a large bf16 GEMM (matrix cores);
   * `extras`: the layer inside an attention block with Q/K/V/O projections
     (autograd, D = H*d) at the headline shape; the other workload shapes (32K forward, the degenerate S = N
-    2K forward, 1M forward+backward) and the pages' own operating points
+    2K forward, 1M forward+backward) and the operating points the ablations
+    favour (bitsgeniais post, "Configurações e Velocidade"; gist.science
+    technical summary §4)
     (L = 3, S = N/p^2 + 1536 for p = 4 and 2 at 98K and 512K, p = 4 at 1M),
     throughput only; the operating points reuse the inputs of the workload
     with the same N, H and d.
@@ -373,10 +375,10 @@ def main():
     ap.add_argument("--no-long", action="store_true", help="skip the 512K comparison")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-extras", action="store_true",
-                    help="skip the other workload shapes and the pages' operating points")
+                    help="skip the other workload shapes and the ablations' operating points")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+        print(f"bench.py: the layer runs on one GPU per process; --gpus {args.gpus} is not supported "
               "(the layer is not sharded across GPUs)", file=sys.stderr)
         sys.exit(2)
 

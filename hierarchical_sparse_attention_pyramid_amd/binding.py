@@ -64,7 +64,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     if _lib is not None:
         return _lib
     if not os.path.exists(path):
-        raise RuntimeError(f"{path} is missing: build it with `python __graft_entry__.py` "
+        raise RuntimeError(f"{path} is missing: build it with `python hierarchical_sparse_attention_pyramid_amd/build.py` "
                            "or hierarchical_sparse_attention_pyramid_amd/build.py")
     lib = ctypes.CDLL(path)
     P, S = ctypes.c_void_p, ctypes.c_size_t

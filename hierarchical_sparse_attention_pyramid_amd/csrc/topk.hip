@@ -3,9 +3,10 @@
 // order (score descending, flat index ascending), written in ascending flat
 // order.
 //
-// The pages' kernel is a chunked bitonic network built for K around 1.5K.
-// Here K reaches 32K out of 1.4M candidates per head, so the selection is an
-// exact radix select instead:
+// The gist.science summary (§2.B) and the bitsgeniais post (phase 2) name a
+// fused chunked-bitonic top-K kernel; the operating points they report
+// select k = 1536 candidates.  Here K reaches 32K out of 1.4M candidates per
+// head, so the selection is an exact radix select instead:
 //   1. three histogram passes over the float32 score bits (11 + 11 + 10
 //      bits; scores are non-negative, so their bit patterns order like the
 //      values) find the score T of the K-th candidate and how many

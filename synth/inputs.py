@@ -54,8 +54,10 @@ CONFIGS = {
                               backward=True),
     "long_n1m_bf16": Config("long_n1m_bf16", 5, 1, 16, 1048576, 128, 4, 7, 32768, "bf16",
                             planted=True, backward=True),
-    # The pages' own operating points: L = 3 levels, k = 1536 selected
-    # candidates, so S = N / p^2 + 1536 (the whole coarsest level plus k).
+    # The operating points the ablations favour (bitsgeniais post,
+    # "Configurações e Velocidade"; gist.science technical summary §4):
+    # L = 3 levels, k = 1536 selected candidates, so S = N / p^2 + 1536 (the
+    # whole coarsest level plus k).
     "op_n98k_p4_bf16": Config("op_n98k_p4_bf16", 7, 1, 16, 98304, 64, 4, 3, 98304 // 16 + 1536,
                               "bf16", backward=True),
     "op_n98k_p2_bf16": Config("op_n98k_p2_bf16", 8, 1, 16, 98304, 64, 2, 3, 98304 // 4 + 1536,

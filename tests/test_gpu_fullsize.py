@@ -26,7 +26,7 @@ pytestmark = pytest.mark.gpu
 
 WORKLOADS = ["fwd_n4k_fp32", "fwd_n32k_bf16", "dense_n2k_bf16", "train_n98k_bf16",
              "long_n512k_bf16", "long_n1m_bf16",
-             # the pages' operating points (L = 3, S = N/p^2 + 1536) at 98K; the
+             # the ablations' operating points (L = 3, S = N/p^2 + 1536) at 98K; the
              # 512K and 1M points run the same kernel paths and are timed only
              "op_n98k_p4_bf16", "op_n98k_p2_bf16"]
 
