@@ -106,6 +106,18 @@ def roofline_entry(kind, work, ms, dtype):
             "frac": round(achieved / peak, 4)}
 
 
+def stage_table(cfg, z, stages_ms, ceil):
+    """Per-stage time with its roofline fraction (datasheet and measured)."""
+    work = stage_work(cfg, z)
+    out = {}
+    for k, t in stages_ms.items():
+        kind, w = work[k]
+        out[k] = {"ms": round(t, 4), **roofline_entry(kind, w, t, cfg.dtype)}
+        meas = ceil["copy_GBs"] if kind == "hbm" else ceil["gemm_bf16_TFLOPs"]
+        out[k]["frac_measured"] = round(out[k]["achieved"] / meas, 4)
+    return out
+
+
 def src_hash(fname):
     path = os.path.join(ROOT, "hierarchical_sparse_attention_pyramid_amd", "csrc", fname)
     return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
@@ -403,12 +415,7 @@ def main():
     prof = [lay.profile() for _ in range(args.profile_reps)]
     stages_ms = {k: sorted(p[k] for p in prof)[len(prof) // 2] for k in prof[0]}
     work = stage_work(cfg, lay.z)
-    stages = {}
-    for k, t in stages_ms.items():
-        kind, w = work[k]
-        stages[k] = {"ms": round(t, 4), **roofline_entry(kind, w, t, cfg.dtype)}
-        meas = ceil["copy_GBs"] if kind == "hbm" else ceil["gemm_bf16_TFLOPs"]
-        stages[k]["frac_measured"] = round(stages[k]["achieved"] / meas, 4)
+    stages = stage_table(cfg, lay.z, stages_ms, ceil)
     dom = max((k for k in stages_ms if k in KERNEL_OF_STAGE), key=lambda k: stages_ms[k])
     kname, kfile = KERNEL_OF_STAGE[dom]
     kind, w = work[dom]
@@ -431,7 +438,8 @@ def main():
         ll = Layer(lcfg, torch, lb)
         l_fb = time_fn(torch, ll.step, max(3, args.steps // 4), 2)
         l_f = time_fn(torch, ll.forward, max(3, args.steps // 4), 1)
-        lprof = ll.profile()
+        lprofs = [ll.profile() for _ in range(3)]
+        lprof = {k: sorted(pr[k] for pr in lprofs)[1] for k in lprofs[0]}  # median of 3
         log(f"[bench] {lcfg.name}: forward {l_f:.2f} ms, forward+backward {l_fb:.2f} ms")
         d_f, d_fb, d_flops = dense_times(torch, lb, ll, args.dense_steps, 1)
         long_ctx = {
@@ -439,7 +447,7 @@ def main():
             "S": lcfg.S,
             "lighthouse_fwd_ms": round(l_f, 3), "lighthouse_fwdbwd_ms": round(l_fb, 3),
             "lighthouse_fwdbwd_tokens_per_s": round(lcfg.B * lcfg.N / (l_fb * 1e-3), 1),
-            "lighthouse_stage_ms": {k: round(v, 4) for k, v in lprof.items()},
+            "lighthouse_stages": stage_table(lcfg, ll.z, lprof, ceil),
             "dense_fwd_ms": round(d_f, 2), "dense_fwdbwd_ms": round(d_fb, 2),
             "dense_fwd_tflops": round(d_flops / (d_f * 1e-3) / 1e12, 1),
             "speedup_fwd": round(d_f / l_f, 2), "speedup_fwdbwd": round(d_fb / l_fb, 2),
