@@ -118,3 +118,17 @@ def test_misaligned_token_pointer_is_rejected_without_a_gpu(lb):
     shape = lb.make_shape(1, 2, 256, 64, 4, 3, 40, 1)
     st = lib.lh_score(ctypes.byref(shape), 4096 + 8, 4096, 4096, None, 0, None)
     assert st == 1 and b"16-byte aligned" in lib.lh_last_error()
+
+
+@pytest.mark.parametrize("args", [
+    (1, 1, 64 * 64, 64, 64, 2, 64, 1),          # largest pooling factor, p = 64
+    (1, 1, 1 << 15, 64, 2, 16, 2, 1),           # deepest pyramid, L = 16 (coarsest level: 2 entries)
+    (1, 1, 4096, 128, 4, 3, 5376, 0),           # S = M: every entry selected
+    (1, 1, 4096, 128, 4, 3, 256, 0),            # S = n_coarse: K = 0
+    (3, 5, 1000, 64, 10, 4, 1, 1),              # non-power-of-two p, one coarse entry per head
+])
+def test_limit_shapes_are_accepted(lb, args):
+    z = lb.lh_query_sizes(lb.Shape(*args))
+    B, H, N, d, p, L, S, dt = args
+    sizes = O.level_sizes(N, p, L)
+    assert z.M == sum(sizes) and z.K == S - sizes[-1]

@@ -37,6 +37,8 @@ CASES = [
     ("dense_n2k_bf16", 1, 16, 2048, 128, 4, 1, 2048, "bf16"),  # degenerate S = N workload
     ("dense_n8k_d64_bf16", 1, 1, 8192, 64, 4, 1, 8192, "bf16"),  # the 98K workload's S and d
     ("ties_bf16", 1, 2, 1024, 64, 4, 4, 120, "bf16"),         # duplicated rows: equal scores
+    ("p64_bf16", 1, 2, 8192, 64, 64, 3, 400, "bf16"),         # largest pooling factor
+    ("deep_L16_fp32", 1, 1, 32768, 64, 2, 16, 300, "fp32"),   # deepest pyramid (one coarse entry)
 ]
 ids = [c[0] for c in CASES]
 _cache: dict = {}
