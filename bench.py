@@ -107,7 +107,9 @@ def roofline_entry(kind, work, ms, dtype):
 
 
 def stage_table(cfg, z, stages_ms, ceil):
-    """Per-stage time with its roofline fraction (datasheet and measured)."""
+    """Per-stage time with its roofline fraction (datasheet and measured).
+    The dQ pass also reports the fraction of the products it executes (dQ plus
+    the recomputed QK^T and dP: three times its algorithmic flops)."""
     work = stage_work(cfg, z)
     out = {}
     for k, t in stages_ms.items():
@@ -115,6 +117,8 @@ def stage_table(cfg, z, stages_ms, ceil):
         out[k] = {"ms": round(t, 4), **roofline_entry(kind, w, t, cfg.dtype)}
         meas = ceil["copy_GBs"] if kind == "hbm" else ceil["gemm_bf16_TFLOPs"]
         out[k]["frac_measured"] = round(out[k]["achieved"] / meas, 4)
+        if k == "attention_dq":
+            out[k]["frac_executed"] = round(3 * out[k]["frac"], 4)
     return out
 
 
