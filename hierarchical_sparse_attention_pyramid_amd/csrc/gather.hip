@@ -22,11 +22,12 @@
 // staged in LDS (every stride-th entry), then quarters that window in global
 // memory (three pivots per round trip; `sel` is small and stays cached) and
 // counts the last <= 16 entries directly.  The source rows are loaded before
-// the searches (they follow from the entries alone) and stored after them.  The same block writes pos for the
-// flat range from after the previous block's last entry to its own last
-// entry (to C for the last block, the whole candidate range split evenly
-// when K = 0): -1 everywhere first, then, after those stores have completed
-// and a barrier, the positions of its entries.
+// the searches (they follow from the entries alone) and stored after them.
+// The same block writes pos for the flat range from after the previous
+// block's last entry to its own last entry (to C for the last block; the
+// whole candidate range split evenly when K = 0): -1 everywhere first, then,
+// after those stores have completed and a barrier, the positions of its
+// entries.
 #include "kernels.h"
 
 namespace lh {
