@@ -20,6 +20,8 @@
 // Backward: a key-block pass (dK, dV; keys stationary) and a query-block pass
 // (dQ; queries stationary), both atomic-free, recomputing P from the stored
 // log-sum-exp.
+#include <type_traits>
+
 #include "kernels.h"
 
 // Forward tiling (queries per wave, waves per workgroup, minimum waves per
@@ -507,17 +509,20 @@ __global__ __launch_bounds__(256) void attn_delta(const float* __restrict__ O, c
   const int rgs = 256 / lpr;
   const int lane = threadIdx.x % lpr;
   const int64_t row = (int64_t)blockIdx.x * rgs + threadIdx.x / lpr;
-  float s = 0.f;
+  // float64 for float32 storage (that path keeps every dot product in
+  // float64: the backward subtracts delta from dP for each key)
+  using Acc = typename std::conditional<std::is_same<T, float>::value, double, float>::type;
+  Acc s = 0;
   if (row < rows) {
     float o[8], g[8];
     Row8<float>::load(O + row * d + 8 * lane, o);
     Row8<T>::load(dO + row * d + 8 * lane, g);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) s += o[e] * g[e];
+    for (int e = 0; e < 8; ++e) s += (Acc)o[e] * (Acc)g[e];
   }
   for (int off = lpr >> 1; off >= 1; off >>= 1) s += __shfl_xor(s, off);
   if (row < rows && lane == 0) {
-    delta[row] = s;
+    delta[row] = (float)s;
     if (lse2) lse2[row] = LSE[row] * kLog2e;
   }
 }
