@@ -1,13 +1,14 @@
-"""Seeded sweep of small random configurations through the whole layer
+"""Seeded sweep of random configurations through the whole layer
 (lh_forward + lh_backward) against the oracle.
 
 The hand-picked parity cases pin specific edge cases; this sweep draws
-shapes the library accepts at random (fixed seed, so the list is the same on
-every run): p from 2 to 9 (powers of two and not), L from 1 to 5, S anywhere
-in [N/p^(L-1), M], d in {64, 128}, fp32 and bf16, B and H in 1..3, and packed
-or strided token layouts.  Every configuration is compared at the layer's
-bar: selection, maps bit-exact; out and dq, dk, dv within the float
-tolerances.  Inputs come from the shared seeded generator.
+shapes the library accepts at random (fixed seeds, so the list is the same
+on every run): p from 2 to 9 (powers of two and not), L from 1 to 5, S
+anywhere in [N/p^(L-1), M], d in {64, 128}, fp32 and bf16, B and H in 1..3,
+packed or strided token layouts; plus eight larger shapes (N up to 16K, S up
+to 4K).  Every configuration is compared at the layer's bar: selection and
+maps bit-exact; out and dq, dk, dv within the float tolerances.  Inputs come
+from the shared seeded generator.
 """
 from __future__ import annotations
 
@@ -46,7 +47,34 @@ def draw_configs(n: int, seed: int = 20261203):
     return out
 
 
-CONFIGS = draw_configs(24)
+def draw_large_configs(n: int, seed: int = 20261204):
+    """Larger shapes (several top-K slices and gather blocks per head, many
+    attention tiles): N in [2048, 16384], B = H = 1, S up to 4096."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        p = int(rng.integers(2, 9))
+        L = int(rng.integers(2, 7))
+        if p ** (L - 1) > 4096:
+            continue
+        base = p ** (L - 1)
+        N = base * int(rng.integers(max(1, 2048 // base), 16384 // base + 1))
+        if N < 2048 or N > 16384:
+            continue
+        sizes = O.level_sizes(N, p, L)
+        M, nc = sum(sizes), sizes[-1]
+        if nc > 4096:
+            continue
+        S = int(rng.integers(nc, min(M, 4096) + 1))
+        d = int(rng.choice([64, 128]))
+        dt = str(rng.choice(["fp32", "bf16"]))
+        strided = bool(rng.integers(0, 2))
+        out.append((f"big{len(out):02d}_p{p}_L{L}_N{N}_S{S}_d{d}_{dt}{'_str' if strided else ''}",
+                    1, 1, N, d, p, L, S, dt, strided))
+    return out
+
+
+CONFIGS = draw_configs(24) + draw_large_configs(8)
 
 
 @pytest.mark.parametrize("cfg", CONFIGS, ids=[c[0] for c in CONFIGS])
