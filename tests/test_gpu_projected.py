@@ -15,10 +15,12 @@ from tests.helpers import check_close, to_f64
 pytestmark = pytest.mark.gpu
 
 CASES = [
-    # name, N, D, H, d, p, L, S, dtype
-    ("block_bf16", 2048, 256, 4, 64, 4, 3, 300, "bf16"),
-    ("block_d128_bf16", 1024, 256, 2, 128, 4, 4, 200, "bf16"),
-    ("block_fp32", 256, 128, 2, 64, 4, 3, 48, "fp32"),
+    # name, N, D, H, d, p, L, S, dtype, B
+    ("block_bf16", 2048, 256, 4, 64, 4, 3, 300, "bf16", 1),
+    ("block_d128_bf16", 1024, 256, 2, 128, 4, 4, 200, "bf16", 1),
+    ("block_fp32", 256, 128, 2, 64, 4, 3, 48, "fp32", 1),
+    # two batch elements (packed projections with a batch stride), model width != H*d
+    ("block_b2_D320_bf16", 1296, 320, 3, 64, 6, 3, 250, "bf16", 2),
 ]
 
 
@@ -31,27 +33,33 @@ def dev(a, dtype):
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
 def test_block_matches_oracle(case, gpu_lib):
     from hierarchical_sparse_attention_pyramid_amd.layer import LighthouseAttention
-    name, N, D, H, d, p, L, S, dt = case
-    print(f"[gpu-block] {name}: N={N} D={D} H={H} d={d} p={p} L={L} S={S} {dt}", flush=True)
+    name, N, D, H, d, p, L, S, dt, B = case
+    print(f"[gpu-block] {name}: B={B} N={N} D={D} H={H} d={d} p={p} L={L} S={S} {dt}", flush=True)
     seed = 500 + 10 * [c[0] for c in CASES].index(name)
-    x = synth.block_tensor(seed, (N, D), dt)
+    xs = [synth.block_tensor(seed + 7 * b, (N, D), dt) for b in range(B)]
     ws = [synth.block_tensor(seed + 1 + i, (H * d, D), dt, D ** -0.5) for i in range(3)]
     wo = synth.block_tensor(seed + 4, (D, H * d), dt, (H * d) ** -0.5)
-    dy = synth.block_tensor(seed + 5, (N, D), dt)
+    dys = [synth.block_tensor(seed + 5 + 7 * b, (N, D), dt) for b in range(B)]
 
     tdt = torch.bfloat16 if dt == "bf16" else torch.float32
     m = LighthouseAttention(D, H, d, p, L, S, dtype=tdt)
     with torch.no_grad():
         for prm, a in zip((m.wq, m.wk, m.wv, m.wo), (*ws, wo)):
             prm.copy_(dev(a, dt))
-    xt = dev(x, dt)[None].requires_grad_(True)
+    xt = torch.stack([dev(x, dt) for x in xs]).requires_grad_(True)
     y = m(xt)
-    y.backward(dev(dy, dt)[None])
+    y.backward(torch.stack([dev(g, dt) for g in dys]))
     torch.cuda.synchronize()
 
-    yr, cache = P.projected_forward(x, *ws, wo, H, p, L, S, dt)
-    gr = P.projected_backward(dy, cache, dt)
-    check_close(to_f64(y[0]), O.to_f64(yr, dt), dt, "block output")
-    for got, ref, what in zip((xt.grad[0], m.wq.grad, m.wk.grad, m.wv.grad, m.wo.grad), gr,
-                              ("dx", "dWq", "dWk", "dWv", "dWo")):
-        check_close(to_f64(got), O.to_f64(ref, dt), dt, what)
+    # per batch element: output and dx; weight gradients sum over the batch
+    gw = [0.0] * 4
+    for b in range(B):
+        yr, cache = P.projected_forward(xs[b], *ws, wo, H, p, L, S, dt)
+        gr = P.projected_backward(dys[b], cache, dt)
+        check_close(to_f64(y[b]), O.to_f64(yr, dt), dt, f"block output [{b}]")
+        check_close(to_f64(xt.grad[b]), O.to_f64(gr[0], dt), dt, f"dx [{b}]")
+        for i in range(4):
+            gw[i] = gw[i] + O.to_f64(gr[1 + i], dt)
+    for got, ref, what in zip((m.wq.grad, m.wk.grad, m.wv.grad, m.wo.grad), gw,
+                              ("dWq", "dWk", "dWv", "dWo")):
+        check_close(to_f64(got), ref, dt, what)
