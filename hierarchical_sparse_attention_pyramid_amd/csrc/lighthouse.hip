@@ -125,6 +125,8 @@ lh_status make_plan(const lh_shape* s, Plan& P) {
   const int64_t BH = s->B * s->H;
   if (BH * M >= (int64_t(1) << 31) || M * s->d >= (int64_t(1) << 31))
     return fail(LH_EUNSUPPORTED, "B*H*M must stay below 2^31");
+  if (BH > 65535)  // the per-head kernels put B*H on the grid's y dimension
+    return fail(LH_EUNSUPPORTED, "B*H above 65535 is not supported");
   if (s->S < nc || s->S > M)
     return fail(LH_EINVAL, "S must satisfy N/p^(L-1) <= S <= M (number of pyramid entries)");
   if (s->H >= (int64_t(1) << 31)) return fail(LH_EUNSUPPORTED, "H must stay below 2^31");

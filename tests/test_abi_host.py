@@ -62,6 +62,7 @@ def test_sizes_match_geometry(lb, N, p, L, S):
     ((1, 1, 64, 64, 4, 3, 20, 7), 1),         # unknown dtype
     ((0, 1, 64, 64, 4, 3, 20, 1), 1),         # empty batch
     ((1, 4096, 1 << 20, 64, 4, 3, 1 << 16, 1), 2),  # B*H*M >= 2^31
+    ((256, 256, 64, 64, 4, 3, 20, 1), 2),     # B*H above the grid's y limit
 ])
 def test_bad_shapes_are_rejected(lb, args, status):
     with pytest.raises(lb.LighthouseError) as ei:
