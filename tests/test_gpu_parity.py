@@ -39,6 +39,7 @@ CASES = [
     ("ties_bf16", 1, 2, 1024, 64, 4, 4, 120, "bf16"),         # duplicated rows: equal scores
     ("p64_bf16", 1, 2, 8192, 64, 64, 3, 400, "bf16"),         # largest pooling factor
     ("deep_L16_fp32", 1, 1, 32768, 64, 2, 16, 300, "fp32"),   # deepest pyramid (one coarse entry)
+    ("zeros_bf16", 1, 2, 1024, 64, 4, 4, 200, "bf16"),        # all-zero q, k, v: every score tied
 ]
 ids = [c[0] for c in CASES]
 _cache: dict = {}
@@ -48,6 +49,8 @@ def gen(case, tensor, seed=900):
     name, B, H, N, d, p, L, S, dt = case
     arr = np.stack([np.stack([synth.head_tensor(seed + CASES.index(case), tensor, b, h, N, d)
                               for h in range(H)]) for b in range(B)])
+    if name.startswith("zeros") and tensor != "dout":
+        arr = np.zeros_like(arr)
     if name.startswith("ties") and tensor != "dout":
         # repeat blocks of 8 rows: many exact score ties, within and across levels
         arr = np.repeat(arr[:, :, ::8], 8, axis=2)
