@@ -1,4 +1,5 @@
-"""Build the Lighthouse HIP library in-tree: liblighthouse.so next to this file.
+"""Build the Lighthouse HIP library in-tree: liblighthouse.so next to this file,
+and the standalone C-ABI program tests/c_abi/lh_step that the tests run.
 
 Every source is compiled for gfx950 only.  Packed-fp32 instructions are
 disabled (`-Xclang -target-feature -Xclang -packed-fp32-ops`): the compiler
@@ -17,6 +18,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "liblighthouse.so")
+STEP_SRC = os.path.join(ROOT, "tests", "c_abi", "lh_step.cpp")
+STEP_BIN = os.path.join(ROOT, "tests", "c_abi", "lh_step")
 
 SOURCES = ["lighthouse.hip", "pyramid.hip", "topk.hip", "gather.hip", "scatter.hip",
            "attention_bf16.hip", "attention_f32.hip"]
@@ -48,6 +51,16 @@ def build(verbose: bool = True) -> str:
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}")
+    if os.path.exists(STEP_SRC):
+        # host program linked against the library; found at run time relative to itself
+        rpath = "-Wl,-rpath,$ORIGIN/../../" + os.path.basename(HERE)
+        cmd = [HIPCC, "--offload-arch=gfx950", "-O2", "-std=c++17", "-I", INCLUDE, STEP_SRC,
+               "-o", STEP_BIN, "-L", HERE, "-llighthouse", rpath]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"building {STEP_SRC} failed:\n{r.stderr}")
+        if verbose:
+            print(f"built {STEP_BIN}")
     return LIB
 
 
