@@ -1,4 +1,7 @@
-"""Non-finite inputs: NaN and infinity rows in q, k, v.
+"""Robustness: non-finite inputs, and concurrent use from several host
+threads.
+
+Non-finite inputs: NaN and infinity rows in q, k, v.
 
 The values that come out are unspecified for such inputs (the header says
 so), but the maps must stay valid, since every later stage indexes memory
@@ -52,3 +55,49 @@ def test_non_finite_rows_keep_the_maps_valid(kind, dt, gpu_lib):
         mask = np.ones(M, bool)
         mask[sub_idx] = False
         assert np.all(pos[mask] == -1)
+
+
+def test_concurrent_host_threads_on_separate_streams(gpu_lib):
+    """Four host threads run whole steps at the same time, each on its own
+    stream with its own buffers (ctypes releases the GIL during the calls):
+    every result equals the one-thread run bit for bit.  The library keeps
+    no state between calls except each thread's error message."""
+    import threading
+    lb = gpu_lib
+    B, H, N, d, p, L, S = 1, 2, 2048, 64, 4, 4, 300
+    host = {t: np.stack([synth.head_tensor(41, t, 0, h, N, d) for h in range(H)])[None]
+            for t in ("q", "k", "v", "dout")}
+    dev = {t: torch.from_numpy(a).cuda().to(torch.bfloat16) for t, a in host.items()}
+    shape = lb.make_shape(B, H, N, d, p, L, S, torch.bfloat16)
+
+    def step(stream):
+        bufs = lb.LayerBuffers(shape)
+        z = bufs.sizes
+        ws = lb.workspace(max(z.ws_forward, z.ws_backward))
+        out, dq, dk, dv = (torch.empty_like(dev["q"]) for _ in range(4))
+        torch.cuda.synchronize()
+        for _ in range(3):
+            lb.lh_forward(shape, dev["q"], dev["k"], dev["v"], out, bufs, ws, stream)
+            lb.lh_backward(shape, dev["dout"], bufs, dq, dk, dv, ws, stream)
+        stream.synchronize()
+        return [t.cpu() for t in (out, dq, dk, dv, bufs.sel, bufs.pos)]
+
+    ref = step(torch.cuda.Stream())
+    results, errors = [None] * 4, []
+
+    def worker(i):
+        try:
+            results[i] = step(torch.cuda.Stream())
+        except Exception as e:  # noqa: BLE001 - reported below
+            errors.append(repr(e))
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(4)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=120)
+    assert not errors, errors
+    for r in results:
+        assert r is not None
+        for a, b in zip(r, ref):
+            assert torch.equal(a, b)
