@@ -1,5 +1,5 @@
-"""Robustness: non-finite inputs, and concurrent use from several host
-threads.
+"""Robustness: non-finite inputs, concurrent use from several host threads,
+and a large number of heads.
 
 Non-finite inputs: NaN and infinity rows in q, k, v.
 
@@ -17,6 +17,7 @@ import torch
 
 from oracle import lighthouse as O
 from synth import inputs as synth
+from tests.helpers import check_close, to_device, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -101,3 +102,29 @@ def test_concurrent_host_threads_on_separate_streams(gpu_lib):
         assert r is not None
         for a, b in zip(r, ref):
             assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "fp32"])
+def test_many_heads(dt, gpu_lib):
+    """B*H = 4096 heads of a short sequence (the per-head kernels put B*H on
+    the grid's y dimension, the attention kernels flatten it with the query
+    or key blocks): 16 sampled heads against the oracle."""
+    lb = gpu_lib
+    B, H, N, d, p, L, S = 64, 64, 256, 64, 4, 3, 40
+    print(f"[robust] many heads {dt}", flush=True)
+    rng = np.random.default_rng(5)
+    a = {t: rng.standard_normal((B, H, N, d), dtype=np.float32) for t in ("q", "k", "v", "dout")}
+    host = {t: synth.bf16_bits_from_f32(x) if dt == "bf16" else x for t, x in a.items()}
+    dev = {t: to_device(x, dt) for t, x in host.items()}
+    out, bufs, shape = lb.forward(dev["q"], dev["k"], dev["v"], p, L, S)
+    dq, dk, dv = lb.backward(shape, dev["dout"], bufs)
+    torch.cuda.synchronize()
+    for i in rng.choice(B * H, size=16, replace=False):
+        b, h = divmod(int(i), H)
+        f = O.forward_head(host["q"][b, h], host["k"][b, h], host["v"][b, h], p, L, S, dt)
+        np.testing.assert_array_equal(bufs.sel[b, h].cpu().numpy(), f["sel"])
+        np.testing.assert_array_equal(bufs.pos[b, h].cpu().numpy(), f["pos"])
+        check_close(to_f64(out[b, h]), O.to_f64(f["out"], dt), dt, f"out[{b},{h}]")
+        g = O.backward_head(host["dout"][b, h], f, p, L, dt)
+        for nm, got, ref in zip(("dq", "dk", "dv"), (dq, dk, dv), g):
+            check_close(to_f64(got[b, h]), ref, dt, f"{nm}[{b},{h}]")
