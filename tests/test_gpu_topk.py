@@ -1,0 +1,86 @@
+"""GPU parity of lh_topk on score arrays the parity workloads do not produce:
+candidate counts whose histogram blocks cover several slices with a partial
+last block, many exact ties at the threshold (the cut falls inside a run of
+equal scores that spans slices), every candidate tied, K = 1, K = C, and a
+head whose scores decrease with the flat index (the K selected candidates are
+the first K).
+
+The expected selection is the oracle's topk (strict order: score descending,
+flat index ascending), compared bit for bit.  sel is pre-filled with a
+sentinel, so every slot must be written.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import lighthouse as O
+
+pytestmark = pytest.mark.gpu
+
+SENTINEL = 0x5A5A5A5A
+
+
+def inherited(level0: np.ndarray, p: int, L: int) -> np.ndarray:
+    """Flat scores of all levels: coarser entries take the max of their children."""
+    lv = [level0.astype(np.float32)]
+    for _ in range(1, L):
+        lv.append(lv[-1].reshape(-1, p).max(axis=1))
+    return np.concatenate(lv)
+
+
+def head_scores(kind: str, N: int, d: int, p: int, L: int, rng) -> np.ndarray:
+    if kind == "norms":  # like the layer: |q| + |k| with log-normal per-token scales
+        c = np.sqrt(d - 0.5)
+        x = (np.exp(0.5 * rng.standard_normal(N)) * (c + 0.707 * rng.standard_normal(N)) +
+             np.exp(0.5 * rng.standard_normal(N)) * (c + 0.707 * rng.standard_normal(N)))
+        return inherited(x, p, L)
+    if kind == "few_values":  # 7 distinct values: long runs of ties everywhere
+        return inherited(rng.integers(0, 7, size=N).astype(np.float32) * 0.25 + 1.0, p, L)
+    if kind == "all_equal":
+        return inherited(np.full(N, 3.5, np.float32), p, L)
+    if kind == "decreasing":  # every level strictly decreasing in the flat index
+        M = sum(O.level_sizes(N, p, L))
+        return np.linspace(1000.0, 1.0, M, dtype=np.float32)
+    raise ValueError(kind)
+
+
+# name, N, d, p, L, K (None: C), score kinds of the heads
+CASES = [
+    # C = 305,000 candidates: 75 slices of 4096, histogram blocks of 2 slices, the last with 1
+    ("ragged_blocks", 305000, 64, 2, 2, 20000, ("norms", "few_values")),
+    # C = 510,000: 125 slices, blocks of 2 (63 blocks, the last with 1); ties cut inside
+    # runs spanning slices
+    ("ties_many_slices", 510000, 64, 4, 2, 50000, ("few_values", "norms")),
+    ("all_equal", 262144, 64, 4, 3, 12345, ("all_equal",)),
+    ("k_one", 65536, 64, 4, 4, 1, ("norms", "few_values")),
+    ("k_all", 65536, 64, 4, 4, None, ("norms",)),
+    ("decreasing", 131072, 64, 2, 5, 30000, ("decreasing",)),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_topk_matches_oracle(case, gpu_lib):
+    lb = gpu_lib
+    name, N, d, p, L, K, kinds = case
+    rng = np.random.default_rng(900 + CASES.index(case))
+    sizes = O.level_sizes(N, p, L)
+    M, nc = sum(sizes), sizes[-1]
+    C = M - nc
+    K = C if K is None else K
+    S = K + nc
+    H = len(kinds)
+    print(f"[topk] case {name}: N={N} p={p} L={L} C={C} K={K} heads={kinds}", flush=True)
+    score = np.stack([head_scores(k, N, d, p, L, rng) for k in kinds])[None]
+    assert score.shape == (1, H, M)
+    shape = lb.make_shape(1, H, N, d, p, L, S, torch.bfloat16)
+    z = lb.lh_query_sizes(shape)
+    assert (z.M, z.C, z.K) == (M, C, K)
+    g_score = torch.from_numpy(score).cuda()
+    g_sel = torch.full((1, H, K), SENTINEL, dtype=torch.int32, device="cuda")
+    lb.lh_topk(shape, g_score, g_sel, lb.workspace(z.ws_topk))
+    torch.cuda.synchronize()
+    for h in range(H):
+        want = O.topk(score[0, h], N, p, L, S)
+        np.testing.assert_array_equal(g_sel[0, h].cpu().numpy(), want, err_msg=f"{name} head {h}")
