@@ -699,16 +699,17 @@ struct BwdQCfg {
 };
 
 // dS^T of a 32-key x 32-query slice in B-operand chunks (query column per
-// lane); lse2 = lse * log2(e) and dl = rowsum(dO*O) of the lane's query.
+// lane); lse2 = lse * log2(e) of the lane's query, and dpacc already holds
+// dP^T - rowsum(dO*O) (its products accumulate onto -rowsum).
 template <bool kMask>
 __device__ __forceinline__ void q_weights(const f32x16& sacc, const f32x16& dpacc, float lse2,
-                                          float dl, float sl2, int kbase, int h, int query,
+                                          float sl2, int kbase, int h, int query,
                                           bf16x8 (&dsch)[2]) {
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     float p = fexp2(__builtin_fmaf(sacc[i], sl2, -lse2));
     if (kMask && kbase + 8 * (i >> 2) + 4 * h + (i & 3) > query) p = 0.f;
-    dsch[i >> 3][i & 7] = static_cast<__bf16>(p * (dpacc[i] - dl));
+    dsch[i >> 3][i & 7] = static_cast<__bf16>(p * dpacc[i]);
   }
 }
 
@@ -750,6 +751,11 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void attn_bwd_dq_bf16(
   f32x16 dqa[D / 32];
 #pragma unroll
   for (int mb = 0; mb < D / 32; ++mb) dqa[mb] = zero16();
+  // the dP^T products start from -rowsum(dO*O) of the lane's query (the lane
+  // is fixed for the whole pass), which saves a subtraction per weight
+  f32x16 negdl;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) negdl[i] = -dl;
 
   for (int kt = 0; kt < ntiles; ++kt) {
     const int k0 = kt * C::kKT;
@@ -766,7 +772,7 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void attn_bwd_dq_bf16(
     for (int kb = 0; kb < 2; ++kb) {
       const int kbase = k0 + kb * 32;
       if (kbase > qw0 + 31) continue;
-      f32x16 sacc = zero16(), dpacc = zero16();
+      f32x16 sacc = zero16(), dpacc = negdl;
 #pragma unroll
       for (int dc = 0; dc < D / 16; ++dc) {
         sacc = mfma32(lds_rows<D>(sKV, lk, kb * 32, dc), qreg[dc], sacc);
@@ -774,9 +780,9 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void attn_bwd_dq_bf16(
       }
       bf16x8 dsch[2];
       if (kbase + 31 > qw0)  // diagonal slice (wave-uniform)
-        q_weights<true>(sacc, dpacc, lse2, dl, sl2, kbase, h, query, dsch);
+        q_weights<true>(sacc, dpacc, lse2, sl2, kbase, h, query, dsch);
       else
-        q_weights<false>(sacc, dpacc, lse2, dl, sl2, kbase, h, query, dsch);
+        q_weights<false>(sacc, dpacc, lse2, sl2, kbase, h, query, dsch);
 #pragma unroll
       for (int c = 0; c < 2; ++c)
 #pragma unroll
