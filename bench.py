@@ -361,24 +361,33 @@ def cpu_single_thread(names):
     return out
 
 
-def cpu_baseline(cfg):
-    """The oracle as it stands, on one head of the headline workload, scaled to
-    the whole layer (all B*H heads)."""
+def cpu_baseline(cfg, budget_s=10.0):
+    """The oracle as it stands, forward+backward on heads (0, 0), (0, 1), ...
+    of the headline workload until about `budget_s` seconds of oracle time
+    (or every head) are spent, scaled to the whole layer (all B*H heads).
+    Input generation is not timed."""
     from threadpoolctl import threadpool_info
 
     from oracle import lighthouse as O
     from synth import inputs as synth
-    x = synth.make_inputs(cfg, tensors=("q", "k", "v", "dout"), heads=[(0, 0)])
-    t0 = time.perf_counter()
-    f = O.forward_head(x["q"][0], x["k"][0], x["v"][0], cfg.p, cfg.L, cfg.S, cfg.dtype)
-    O.backward_head(x["dout"][0], f, cfg.p, cfg.L, cfg.dtype)
-    t = time.perf_counter() - t0
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     heads = cfg.B * cfg.H
-    return {"value": round(cfg.B * cfg.N / (t * heads), 2), "unit": "tokens/s", "cores": threads,
-            "kind": "oracle",
-            "sample": f"head (b=0,h=0) of {cfg.name}, forward+backward, {t:.2f}s; "
-                      f"layer time = {heads} x head time; {os.cpu_count()} host cpus visible"}
+    t, done = 0.0, 0
+    for bh in range(heads):
+        b, h = divmod(bh, cfg.H)
+        x = synth.make_inputs(cfg, tensors=("q", "k", "v", "dout"), heads=[(b, h)])
+        t0 = time.perf_counter()
+        f = O.forward_head(x["q"][0], x["k"][0], x["v"][0], cfg.p, cfg.L, cfg.S, cfg.dtype)
+        O.backward_head(x["dout"][0], f, cfg.p, cfg.L, cfg.dtype)
+        t += time.perf_counter() - t0
+        done += 1
+        if t >= budget_s:
+            break
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"value": round(cfg.B * cfg.N * done / (t * heads), 2), "unit": "tokens/s",
+            "cores": threads, "kind": "oracle",
+            "sample": f"heads 0..{done - 1} (of {heads}) of {cfg.name}, forward+backward, "
+                      f"{t:.1f}s of oracle time; layer time = {heads}/{done} x that; "
+                      f"{os.cpu_count()} host cpus visible"}
 
 
 def main():
