@@ -37,7 +37,14 @@
 #define LH_FWD128_MINW 2
 #endif
 // Backward: waves per workgroup of the key-block (dK, dV) and query-block
-// (dQ) passes; every wave owns 32 keys or 32 queries.
+// (dQ) passes; every wave owns 32 keys or 32 queries.  d = 64 key-block
+// passes with at least LH_BKV64_WIDE_MIN workgroups of LH_BKV64_WIDE waves
+// use those (wider workgroups share each staged query tile among more keys);
+// smaller grids keep LH_BKV64_WAVES, so that enough workgroups exist.
+#ifndef LH_BKV64_WIDE
+#define LH_BKV64_WIDE 8
+#define LH_BKV64_WIDE_MIN 256
+#endif
 #ifndef LH_BKV64_WAVES
 #define LH_BKV64_WAVES 4
 #define LH_BKV64_MINW 2
@@ -873,12 +880,20 @@ hipError_t launch_attn_bwd(const void* q, const void* k, const void* v, const fl
   const auto V = static_cast<const __bf16*>(v);
   const auto G = static_cast<const __bf16*>(dout);
   if (d == 64) {
-    using C1 = BwdKVCfg<64, LH_BKV64_WAVES>;
-    const int64_t nb = (S + C1::kKB - 1) / C1::kKB;
-    const bool pr = LH_PAIR_BKV64 && pair_blocks(nb, BH);
-    attn_bwd_dkdv_bf16<64, LH_BKV64_WAVES, LH_BKV64_MINW>
-        <<<dim3((unsigned)causal_grid(nb, BH, pr)), 64 * LH_BKV64_WAVES, 0, st>>>(
-            Q, K, V, G, lse2, delta, dk, dv, (int)S, sl2, scale, pr ? 1 : 0);
+    auto dkdv64 = [&](auto waves) {
+      constexpr int W = decltype(waves)::value;
+      using C1 = BwdKVCfg<64, W>;
+      const int64_t nb = (S + C1::kKB - 1) / C1::kKB;
+      const bool pr = LH_PAIR_BKV64 && pair_blocks(nb, BH);
+      attn_bwd_dkdv_bf16<64, W, LH_BKV64_MINW>
+          <<<dim3((unsigned)causal_grid(nb, BH, pr)), 64 * W, 0, st>>>(
+              Q, K, V, G, lse2, delta, dk, dv, (int)S, sl2, scale, pr ? 1 : 0);
+    };
+    const int64_t wide_kb = BwdKVCfg<64, LH_BKV64_WIDE>::kKB;
+    if ((S + wide_kb - 1) / wide_kb * BH >= LH_BKV64_WIDE_MIN)
+      dkdv64(std::integral_constant<int, LH_BKV64_WIDE>{});
+    else
+      dkdv64(std::integral_constant<int, LH_BKV64_WAVES>{});
   } else {
     using C1 = BwdKVCfg<128, LH_BKV128_WAVES>;
     const int64_t nb = (S + C1::kKB - 1) / C1::kKB;
