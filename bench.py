@@ -490,7 +490,7 @@ def main():
     cpu = None if args.no_cpu else cpu_baseline(cfg)
     if cpu:
         log(f"[bench] cpu oracle: {cpu['value']} tokens/s ({cpu['sample']})")
-        cpu["single_thread"] = cpu_single_thread(("fwd_n4k_fp32", "fwd_n32k_bf16"))
+        cpu["single_thread"] = cpu_single_thread(("fwd_n4k_fp32", "fwd_n32k_bf16", "train_n98k_bf16"))
         log(f"[bench] cpu oracle, one thread: {cpu['single_thread']}")
 
     rec = {
