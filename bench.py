@@ -74,7 +74,8 @@ def stage_work(cfg, z):
     Attention flops count causal (i, j <= i) pairs: forward 2 matmuls, the
     backward 5 (recompute of QK^T, dP, dV, dK, dQ), split as 4 in the
     key-block pass and 1 (dQ) in the query-block pass; the query-block pass
-    also recomputes QK^T and dP, which is not counted."""
+    also recomputes QK^T and dP, which is not counted.  With bf16 storage the
+    query-block pass also forms rowsum(dO*O) (no kernel of its own then)."""
     BH = cfg.B * cfg.H
     N, d, S, M = cfg.N, cfg.d, cfg.S, z.M
     e = 2 if cfg.dtype == "bf16" else 4
@@ -114,6 +115,10 @@ def stage_table(cfg, z, stages_ms, ceil):
     out = {}
     for k, t in stages_ms.items():
         kind, w = work[k]
+        if k == "attention_delta" and cfg.dtype == "bf16":
+            # no kernel of its own: the dQ pass forms rowsum(dO*O)
+            out[k] = {"ms": round(t, 4), "in": "attention_dq"}
+            continue
         out[k] = {"ms": round(t, 4), **roofline_entry(kind, w, t, cfg.dtype)}
         meas = ceil["copy_GBs"] if kind == "hbm" else ceil["gemm_bf16_TFLOPs"]
         out[k]["frac_measured"] = round(out[k]["achieved"] / meas, 4)

@@ -502,36 +502,31 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void attn_fwd_bf16(
 
 // ------------------------------------------------------------------ backward
 
-// delta[i] = sum_d dO[i,d] * O[i,d] (float32), one row per d/8-lane group.
-// O is the float32 forward output: rounding it to bf16 first would perturb
-// delta by ~2^-9 |dO||O|, and dS = P (dP - delta) cancels for keys that
-// dominate a row, which would amplify that error in dK and dQ.
-// It also writes lse * log2(e) (lse2), the form the bf16 passes use.
-template <typename T>
-__global__ __launch_bounds__(256) void attn_delta(const float* __restrict__ O, const T* __restrict__ dO,
-                                                  const float* __restrict__ LSE,
-                                                  float* __restrict__ delta, float* __restrict__ lse2,
-                                                  int64_t rows, int d) {
+// delta[i] = sum_d dO[i,d] * O[i,d], one row per d/8-lane group, for the
+// float32 storage path (the bf16 path forms it in its dQ pass), accumulated
+// in float64 like every dot product of that path (the backward subtracts
+// delta from dP for each key).  O is the float32 forward output in both
+// paths: rounding it to bf16 first would perturb delta by ~2^-9 |dO||O|, and
+// dS = P (dP - delta) cancels for keys that dominate a row, which would
+// amplify that error in dK and dQ.
+__global__ __launch_bounds__(256) void attn_delta_f32(const float* __restrict__ O,
+                                                      const float* __restrict__ dO,
+                                                      float* __restrict__ delta, int64_t rows,
+                                                      int d) {
   const int lpr = d / 8;
   const int rgs = 256 / lpr;
   const int lane = threadIdx.x % lpr;
   const int64_t row = (int64_t)blockIdx.x * rgs + threadIdx.x / lpr;
-  // float64 for float32 storage (that path keeps every dot product in
-  // float64: the backward subtracts delta from dP for each key)
-  using Acc = typename std::conditional<std::is_same<T, float>::value, double, float>::type;
-  Acc s = 0;
+  double s = 0;
   if (row < rows) {
     float o[8], g[8];
     Row8<float>::load(O + row * d + 8 * lane, o);
-    Row8<T>::load(dO + row * d + 8 * lane, g);
+    Row8<float>::load(dO + row * d + 8 * lane, g);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) s += (Acc)o[e] * (Acc)g[e];
+    for (int e = 0; e < 8; ++e) s += (double)o[e] * (double)g[e];
   }
   for (int off = lpr >> 1; off >= 1; off >>= 1) s += __shfl_xor(s, off);
-  if (row < rows && lane == 0) {
-    delta[row] = (float)s;
-    if (lse2) lse2[row] = LSE[row] * kLog2e;
-  }
+  if (row < rows && lane == 0) delta[row] = (float)s;
 }
 
 // Stage 64 float32 values (lse or delta of a query tile) into LDS with one
@@ -697,6 +692,9 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void attn_bwd_dkdv_bf16(
 // lse and delta in registers) and walks the key tiles up to its diagonal:
 //   S^T = K Q^T, dP^T = V dO^T      (A = K / V rows from LDS)
 //   dS^T = P^T (dP^T - delta), dQ^T += K^T dS^T (A = transposed reads of K)
+// Every query belongs to one wave of this pass, so the pass also forms its
+// delta = rowsum(dO*O) and lse*log2(e) and writes them for the key-block
+// pass, which runs after it.
 template <int D, int WAVES>
 struct BwdQCfg {
   static constexpr int kQW = 32;
@@ -723,8 +721,9 @@ __device__ __forceinline__ void q_weights(const f32x16& sacc, const f32x16& dpac
 template <int D, int WAVES, int MINW>
 __global__ __launch_bounds__(64 * WAVES, MINW) void attn_bwd_dq_bf16(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
-    const __bf16* __restrict__ dO, const float* __restrict__ LSE2, const float* __restrict__ DELTA,
-    float* __restrict__ dQ, int S, float sl2, float scale, int paired) {
+    const __bf16* __restrict__ dO, const float* __restrict__ O, const float* __restrict__ LSE,
+    float* __restrict__ LSE2, float* __restrict__ DELTA, float* __restrict__ dQ, int S, float sl2,
+    float scale, int paired) {
   using C = BwdQCfg<D, WAVES>;
   __shared__ __attribute__((aligned(1024))) __bf16 sKV[2][2][C::kTile];  // [buffer][K, V]
   const int tid = threadIdx.x, lane = tid & 63;
@@ -753,8 +752,29 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void attn_bwd_dq_bf16(
     qreg[dc] = query < S ? *reinterpret_cast<const bf16x8*>(Q + off + (int64_t)query * D + dc * 16 + 8 * h) : zero8();
     doreg[dc] = query < S ? *reinterpret_cast<const bf16x8*>(dO + off + (int64_t)query * D + dc * 16 + 8 * h) : zero8();
   }
-  const float lse2 = query < S ? LSE2[bh * (int64_t)S + query] : 0.f;
-  const float dl = query < S ? DELTA[bh * (int64_t)S + query] : 0.f;
+  // rowsum(dO*O) and lse*log2(e) of the lane's query, written for the
+  // key-block pass that runs after this one: the two halves of the wave hold
+  // the two halves of the query's dO row
+  float dl = 0.f, lse2 = 0.f;
+  if (query < S) {
+    const float* orow = O + off + (int64_t)query * D + 8 * h;
+#pragma unroll
+    for (int dc = 0; dc < D / 16; ++dc) {
+      const f32x4 a = *reinterpret_cast<const f32x4*>(orow + dc * 16);
+      const f32x4 b = *reinterpret_cast<const f32x4*>(orow + dc * 16 + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        dl = __builtin_fmaf((float)doreg[dc][e], a[e], dl);
+        dl = __builtin_fmaf((float)doreg[dc][4 + e], b[e], dl);
+      }
+    }
+    lse2 = LSE[bh * (int64_t)S + query] * kLog2e;
+  }
+  dl += __shfl_xor(dl, 32);
+  if (query < S && h == 0) {
+    DELTA[bh * (int64_t)S + query] = dl;
+    LSE2[bh * (int64_t)S + query] = lse2;
+  }
   f32x16 dqa[D / 32];
 #pragma unroll
   for (int mb = 0; mb < D / 32; ++mb) dqa[mb] = zero16();
@@ -857,13 +877,13 @@ hipError_t launch_attn_bwd(const void* q, const void* k, const void* v, const fl
   const int64_t rows = S * BH;
   const int rgs = 256 / (d / 8);
   const unsigned dgrid = (unsigned)((rows + rgs - 1) / rgs);
+  // float32: rowsum kernel, key-block pass, query-block pass.  bf16: the
+  // query-block pass forms the rowsum and lse*log2(e) and runs first.  ev[0],
+  // ev[1], ev[2] mark the ends of the rowsum, dK/dV and dQ stages (for bf16
+  // recorded in the order ev[0], ev[2], ev[1]; the rowsum stage is empty).
   const bool f32 = dtype == 0;
   if (f32)
-    attn_delta<float><<<dgrid, 256, 0, st>>>(o, static_cast<const float*>(dout), lse, delta,
-                                             nullptr, rows, d);
-  else
-    attn_delta<__bf16><<<dgrid, 256, 0, st>>>(o, static_cast<const __bf16*>(dout), lse, delta,
-                                              lse2, rows, d);
+    attn_delta_f32<<<dgrid, 256, 0, st>>>(o, static_cast<const float*>(dout), delta, rows, d);
   hipError_t e = hipGetLastError();
   if (e == hipSuccess && ev) e = hipEventRecord(ev[0], st);
   if (e != hipSuccess) return e;
@@ -879,6 +899,24 @@ hipError_t launch_attn_bwd(const void* q, const void* k, const void* v, const fl
   const auto K = static_cast<const __bf16*>(k);
   const auto V = static_cast<const __bf16*>(v);
   const auto G = static_cast<const __bf16*>(dout);
+  if (d == 64) {
+    using C2 = BwdQCfg<64, LH_BQ64_WAVES>;
+    const int64_t nb = (S + C2::kQB - 1) / C2::kQB;
+    const bool pr = LH_PAIR_BQ && pair_blocks(nb, BH);
+    attn_bwd_dq_bf16<64, LH_BQ64_WAVES, LH_BQ64_MINW>
+        <<<dim3((unsigned)causal_grid(nb, BH, pr)), 64 * LH_BQ64_WAVES, 0, st>>>(
+            Q, K, V, G, o, lse, lse2, delta, dq, (int)S, sl2, scale, pr ? 1 : 0);
+  } else {
+    using C2 = BwdQCfg<128, LH_BQ128_WAVES>;
+    const int64_t nb = (S + C2::kQB - 1) / C2::kQB;
+    const bool pr = LH_PAIR_BQ && pair_blocks(nb, BH);
+    attn_bwd_dq_bf16<128, LH_BQ128_WAVES, LH_BQ128_MINW>
+        <<<dim3((unsigned)causal_grid(nb, BH, pr)), 64 * LH_BQ128_WAVES, 0, st>>>(
+            Q, K, V, G, o, lse, lse2, delta, dq, (int)S, sl2, scale, pr ? 1 : 0);
+  }
+  e = hipGetLastError();
+  if (e == hipSuccess && ev) e = hipEventRecord(ev[2], st);
+  if (e != hipSuccess) return e;
   if (d == 64) {
     auto dkdv64 = [&](auto waves) {
       constexpr int W = decltype(waves)::value;
@@ -904,24 +942,6 @@ hipError_t launch_attn_bwd(const void* q, const void* k, const void* v, const fl
   }
   e = hipGetLastError();
   if (e == hipSuccess && ev) e = hipEventRecord(ev[1], st);
-  if (e != hipSuccess) return e;
-  if (d == 64) {
-    using C2 = BwdQCfg<64, LH_BQ64_WAVES>;
-    const int64_t nb = (S + C2::kQB - 1) / C2::kQB;
-    const bool pr = LH_PAIR_BQ && pair_blocks(nb, BH);
-    attn_bwd_dq_bf16<64, LH_BQ64_WAVES, LH_BQ64_MINW>
-        <<<dim3((unsigned)causal_grid(nb, BH, pr)), 64 * LH_BQ64_WAVES, 0, st>>>(
-            Q, K, V, G, lse2, delta, dq, (int)S, sl2, scale, pr ? 1 : 0);
-  } else {
-    using C2 = BwdQCfg<128, LH_BQ128_WAVES>;
-    const int64_t nb = (S + C2::kQB - 1) / C2::kQB;
-    const bool pr = LH_PAIR_BQ && pair_blocks(nb, BH);
-    attn_bwd_dq_bf16<128, LH_BQ128_WAVES, LH_BQ128_MINW>
-        <<<dim3((unsigned)causal_grid(nb, BH, pr)), 64 * LH_BQ128_WAVES, 0, st>>>(
-            Q, K, V, G, lse2, delta, dq, (int)S, sl2, scale, pr ? 1 : 0);
-  }
-  e = hipGetLastError();
-  if (e == hipSuccess && ev) e = hipEventRecord(ev[2], st);
   return e;
 }
 

@@ -564,7 +564,8 @@ static lh_status check_backward_args(const void* dout, const lh_buffers* b, void
 }
 
 // Backward launch sequence; when `ev` is given, ev[i] is recorded after stage
-// i (scatter backward, delta, dK/dV pass, dQ pass, gather backward).
+// i (scatter backward, delta, dK/dV pass, dQ pass, gather backward), in the
+// order the stages run (bf16: the dQ pass, which forms delta, before dK/dV).
 static lh_status run_backward(const Plan& P, const void* dout, const lh_buffers* b, void* dq,
                               void* dk, void* dv, void* ws, hipStream_t st, hipEvent_t* ev) {
   char* w = static_cast<char*>(ws);
@@ -634,9 +635,19 @@ lh_status lh_profile_step(const lh_shape* shape, const void* q, const void* k, c
   hipError_t e = hipEventRecord(ev[0], st);
   if (e == hipSuccess) s = run_forward(P, q, k, v, out, b, ws, st, ev + 1);
   if (e == hipSuccess && s == LH_OK) s = run_backward(P, dout, b, dq, dk, dv, ws, st, ev + 6);
-  if (e == hipSuccess && s == LH_OK) e = hipEventSynchronize(ev[LH_PROFILE_STAGES]);
-  for (int i = 0; e == hipSuccess && s == LH_OK && i < LH_PROFILE_STAGES; ++i)
-    e = hipEventElapsedTime(&ms[i], ev[i], ev[i + 1]);
+  // ev[i + 1] marks the end of stage i; stages run in index order except
+  // that with bf16 storage the dQ pass (8) runs before the dK/dV pass (7)
+  int order[LH_PROFILE_STAGES];
+  for (int i = 0; i < LH_PROFILE_STAGES; ++i) order[i] = i;
+  if (P.dtype == 1) {
+    order[7] = 8;
+    order[8] = 7;
+  }
+  if (e == hipSuccess && s == LH_OK) e = hipEventSynchronize(ev[order[LH_PROFILE_STAGES - 1] + 1]);
+  for (int i = 0; e == hipSuccess && s == LH_OK && i < LH_PROFILE_STAGES; ++i) {
+    const hipEvent_t start = i == 0 ? ev[0] : ev[order[i - 1] + 1];
+    e = hipEventElapsedTime(&ms[order[i]], start, ev[order[i] + 1]);
+  }
   for (int i = 0; i <= LH_PROFILE_STAGES; ++i) hipEventDestroy(ev[i]);
   if (e != hipSuccess) return hip_fail(e, "profile");
   return s;

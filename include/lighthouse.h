@@ -226,6 +226,8 @@ lh_status lh_backward(const lh_shape *shape, const void *dout, const lh_buffers 
  *   0 pyramid + scores   1 top-K            2 gather        3 attention
  *   4 scatter            5 scatter backward 6 rowsum(dO*O)  7 attention dK,dV
  *   8 attention dQ       9 gather+pool backward
+ * With bf16 storage the dQ pass forms rowsum(dO*O) itself and runs before
+ * the dK/dV pass, so stage 6 is empty (about 0 ms).
  * Arguments as for lh_forward / lh_backward; ws must hold
  * max(ws_forward, ws_backward) bytes.  Unlike every other entry point this
  * call waits for the stream before returning. */
