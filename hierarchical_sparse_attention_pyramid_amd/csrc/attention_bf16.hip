@@ -57,8 +57,8 @@
 #define LH_BQ128_MINW 2
 #endif
 
-// Causal pairing per pass (measured: it pays where a launch has few, long
-// workgroups; with d = 64 the extra resident waves of the unpaired grid win).
+// Causal pairing per pass, off by default: measured neutral or slower in every
+// pass (d = 128 key blocks at S = 16K, 32K and 34K: 1.4-9% slower paired).
 #ifndef LH_PAIR_FWD
 #define LH_PAIR_FWD 0
 #endif
@@ -66,7 +66,7 @@
 #define LH_PAIR_BKV64 0
 #endif
 #ifndef LH_PAIR_BKV128
-#define LH_PAIR_BKV128 1
+#define LH_PAIR_BKV128 0
 #endif
 #ifndef LH_PAIR_BQ
 #define LH_PAIR_BQ 0
