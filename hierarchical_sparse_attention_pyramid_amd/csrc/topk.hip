@@ -133,7 +133,8 @@ __device__ void pick(uint32_t* w, int pass, uint32_t& prefix_out, uint32_t& rem_
 }
 
 // This thread's candidates of the block's slice (i0 + tid + 256 r), loaded
-// at once; positions past C hold a bit pattern no later test accepts.
+// at once; positions past C read as 0 and are excluded by the callers' bounds
+// tests.
 __device__ __forceinline__ void load_slice(const float* s, int i0, int C, uint32_t (&u)[kSlice / kThreads]) {
 #pragma unroll
   for (int r = 0; r < kSlice / kThreads; ++r) {
