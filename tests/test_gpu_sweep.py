@@ -119,3 +119,43 @@ def test_random_config_matches_oracle(cfg, gpu_lib):
             g = O.backward_head(host["dout"][b, h], f, p, L, dt)
             for nm, got, ref in zip(("dq", "dk", "dv"), (dq, dk, dv), g):
                 check_close(to_f64(got[b, h]), ref, dt, f"{nm} {where}")
+
+
+# Layer shapes with many heads and long subsequences, so that the d = 64
+# dK/dV pass takes its wide workgroups, with factors whose scatter and
+# gather backward take the generic (not power-of-two) ancestor walk; two
+# sampled heads each, compared in full.
+LARGE_GRID = [
+    # name, B, H, N, d, p, L, S, dtype
+    ("grid_p3_d64", 1, 16, 27 * 1024, 64, 3, 4, 4500, "bf16"),
+    ("grid_p5_d64", 2, 8, 25 * 1200, 64, 5, 3, 4100, "bf16"),
+    ("grid_p3_d128", 1, 16, 27 * 512, 128, 3, 4, 3000, "bf16"),
+]
+
+
+@pytest.mark.parametrize("cfg", LARGE_GRID, ids=[c[0] for c in LARGE_GRID])
+def test_large_grid_layer_matches_oracle(cfg, gpu_lib):
+    lb = gpu_lib
+    name, B, H, N, d, p, L, S, dt = cfg
+    print(f"[sweep] {name}", flush=True)
+    seed = 8000 + LARGE_GRID.index(cfg)
+    host = {}
+    for t in ("q", "k", "v", "dout"):
+        a = np.stack([np.stack([synth.head_tensor(seed, t, b, h, N, d) for h in range(H)])
+                      for b in range(B)])
+        host[t] = synth.bf16_bits_from_f32(a)
+    dev = {t: to_device(a, dt) for t, a in host.items()}
+    out, bufs, shape = lb.forward(dev["q"], dev["k"], dev["v"], p, L, S)
+    dq, dk, dv = lb.backward(shape, dev["dout"], bufs)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(seed)
+    for i in rng.choice(B * H, size=2, replace=False):
+        b, h = divmod(int(i), H)
+        f = O.forward_head(host["q"][b, h], host["k"][b, h], host["v"][b, h], p, L, S, dt)
+        where = f"{name}[{b},{h}]"
+        np.testing.assert_array_equal(bufs.sel[b, h].cpu().numpy(), f["sel"], err_msg=where)
+        np.testing.assert_array_equal(bufs.pos[b, h].cpu().numpy(), f["pos"], err_msg=where)
+        check_close(to_f64(out[b, h]), O.to_f64(f["out"], dt), dt, f"out {where}")
+        g = O.backward_head(host["dout"][b, h], f, p, L, dt)
+        for nm, got, ref in zip(("dq", "dk", "dv"), (dq, dk, dv), g):
+            check_close(to_f64(got[b, h]), ref, dt, f"{nm} {where}")
