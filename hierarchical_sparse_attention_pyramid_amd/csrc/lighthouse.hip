@@ -45,6 +45,11 @@ struct Plan {
 #ifndef LH_POOL_TOKCHUNK
 #define LH_POOL_TOKCHUNK 64
 #endif
+// A pooling workgroup covers at most 32 row groups x 64 rows; the backward
+// pooling kernel stages those rows' positions and their ancestors' (at most
+// as many again for p >= 2, plus one per level) in a fixed LDS cache sized
+// for that bound.
+static_assert(LH_POOL_TOKCHUNK <= 64, "token chunks above 64 rows overflow the position cache");
 
 int lam_max(int p) {
   int lam = 1;
