@@ -90,6 +90,44 @@ def test_l2norm_close_to_float64_norm():
     np.testing.assert_allclose(got, ref, rtol=2 ** -20)
 
 
+def _order_rows(d):
+    """Rows of tests/golden/score_order.json, widened to d elements (the
+    eight values at elements 0, d/8, 2d/8, ...; zeros elsewhere)."""
+    g = json.load(open(os.path.join(GOLDEN, "score_order.json")))
+    out = {}
+    for name, row in g["rows"].items():
+        x = np.zeros(d, np.float32)
+        for m, ex in enumerate(row["x_pow2_exponents"]):
+            if ex is not None:
+                x[m * (d // 8)] = np.float32(2.0 ** ex)
+        out[name] = (x, row)
+    return out
+
+
+@pytest.mark.parametrize("d", [8, 64, 128])
+def test_l2norm_summation_order_golden(d):
+    """The halving-tree order of R4, pinned by hand-derived bit patterns that a
+    sequential or an adjacent-pair summation would not produce."""
+    for name, (x, row) in _order_rows(d).items():
+        got = O.l2norm_f32(x[None])[0].view(np.uint32)
+        assert got == int(row["norm_bits"], 16), (name, d, hex(got))
+        q = np.tile(x, (4, 1))
+        s = O.scores(q, q, 2, 2)               # k = q: score = 2 * norm, exact
+        assert s[0].view(np.uint32) == int(row["score_q_eq_k_bits"], 16), (name, d)
+        assert s[4].view(np.uint32) == s[0].view(np.uint32)   # level 1 inherits the max
+
+
+def test_l2norm_order_golden_separates_the_orders():
+    """The golden's alternative-order bit patterns really differ from the
+    halving tree's, so the pin above would catch either mistake."""
+    for name, (x, row) in _order_rows(8).items():
+        assert row["norm_bits"] != row["sequential_bits"] or \
+            row["norm_bits"] != row["adjacent_pairs_bits"], name
+    rows = _order_rows(8)
+    assert rows["tree_vs_sequential"][1]["sequential_bits"] != rows["tree_vs_sequential"][1]["norm_bits"]
+    assert rows["tree_vs_pairs"][1]["adjacent_pairs_bits"] != rows["tree_vs_pairs"][1]["norm_bits"]
+
+
 def test_golden_tiny_selection():
     g = json.load(open(os.path.join(GOLDEN, "tiny_selection.json")))
     N, p, L, S = g["N"], g["p"], g["L"], g["S"]
