@@ -156,10 +156,12 @@ __host__ __device__ constexpr int toff(int r, int x) {
 // per-tile chunk parts stay live.
 
 // Buffer descriptor (raw, stride 0) of `bytes` bytes from p: loads at
-// offsets >= bytes return zero.
+// offsets >= bytes return zero.  The record count is an unsigned 32-bit
+// field; the host keeps every head's S * d * 2 below 2^32 (M * d < 2^31).
 constexpr int kBufWord3 = 0x00020000;
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, bytes, kBufWord3);
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0,
+                                           __builtin_bit_cast(int, bytes), kBufWord3);
 }
 
 // Asynchronously copy rows [r0, r0 + R) of a [S][D] bf16 tensor into a
@@ -174,7 +176,7 @@ __device__ __forceinline__ void load_tile(const __bf16* src, int S, int r0, __bf
   constexpr int kCPR = D / 8;
   constexpr int kInst = R * kCPR / 64;
   const int rows = S > r0 ? S - r0 : 0;
-  const __amdgpu_buffer_rsrc_t rs = rsrc(src + (int64_t)r0 * D, rows * D * 2);
+  const __amdgpu_buffer_rsrc_t rs = rsrc(src + (int64_t)r0 * D, (uint32_t)rows * (uint32_t)(D * 2));
 #pragma unroll
   for (int n = wave; n < kInst; n += NW) {
     const int p = n * 64 + lane;
@@ -533,7 +535,7 @@ __global__ __launch_bounds__(256) void attn_delta_f32(const float* __restrict__ 
 // direct load (4 bytes per lane); rows >= S read as zero (masked queries).
 __device__ __forceinline__ void load_vec64(const float* src, int S, int r0, float* dst, int lane) {
   const int rows = S > r0 ? S - r0 : 0;
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc(src + r0, rows * 4), (lds_void*)dst, 4, lane * 4, 0,
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc(src + r0, (uint32_t)rows * 4u), (lds_void*)dst, 4, lane * 4, 0,
                                            0, 0);
 }
 

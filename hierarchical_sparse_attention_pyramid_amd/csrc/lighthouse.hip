@@ -128,8 +128,13 @@ lh_status make_plan(const lh_shape* s, Plan& P) {
   }
   const int64_t nc = s->N / pw;
   const int64_t BH = s->B * s->H;
-  if (BH * M >= (int64_t(1) << 31) || M * s->d >= (int64_t(1) << 31))
+  // 32-bit indexing: flat entries of all heads, and one head's M * d
+  // elements (so that S * d * 2 bytes, a buffer-descriptor record count in
+  // the attention kernels, stays below 2^32)
+  if (BH * M >= (int64_t(1) << 31))
     return fail(LH_EUNSUPPORTED, "B*H*M must stay below 2^31");
+  if (M * s->d >= (int64_t(1) << 31))
+    return fail(LH_EUNSUPPORTED, "M*d must stay below 2^31");
   if (BH > 65535)  // the per-head kernels put B*H on the grid's y dimension
     return fail(LH_EUNSUPPORTED, "B*H above 65535 is not supported");
   if (s->S < nc || s->S > M)

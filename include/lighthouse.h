@@ -40,7 +40,8 @@
  *    non-finite score, which the top-K ranks by its bit pattern (as a value
  *    above every finite score); outputs touched by it are not meaningful.
  *  - Shape limits: 2 <= p <= 64, 1 <= L <= 16, N % p^(L-1) == 0,
- *    n_coarse <= S <= M, d in {64, 128}, B*H*M < 2^31, B*H <= 65535 (p > 64 returns
+ *    n_coarse <= S <= M, d in {64, 128}, B*H*M < 2^31, M*d < 2^31 (so one head's
+ *    S*d*2 bytes stay below 2^32), B*H <= 65535 (p > 64 returns
  *    LH_EUNSUPPORTED: the pooling kernels stage a workgroup's positions in
  *    LDS sized for spans of at most 64 rows per pass).
  */

@@ -133,3 +133,22 @@ def test_limit_shapes_are_accepted(lb, args):
     B, H, N, d, p, L, S, dt = args
     sizes = O.level_sizes(N, p, L)
     assert z.M == sum(sizes) and z.K == S - sizes[-1]
+
+
+@pytest.mark.parametrize("N,d,ok", [
+    (1 << 23, 128, True),    # S * d * 2 = 2^31 bytes per head: the attention's buffer
+                             # descriptors take it as an unsigned 32-bit record count
+    (1 << 24, 64, True),     # the same byte count at d = 64
+    (1 << 24, 128, False),   # M * d = 2^31: rejected before any launch
+])
+def test_subsequence_byte_size_limit(lb, N, d, ok):
+    """Largest accepted subsequence: M * d < 2^31, so every head's S * d * 2
+    bytes stays below 2^32 (dense causal attention, L = 1, S = N)."""
+    shape = lb.Shape(1, 1, N, d, 4, 1, N, 1)
+    if ok:
+        z = lb.lh_query_sizes(shape)
+        assert z.bytes_sub == N * d * 2 and z.bytes_sub < 1 << 32
+    else:
+        with pytest.raises(lb.LighthouseError) as ei:
+            lb.lh_query_sizes(shape)
+        assert ei.value.status == 2
