@@ -34,9 +34,18 @@ reading list):
   R9  causal order of the subsequence: by (end token, level) ascending, where
       end(l, j) = (j+1)*p**l - 1.
   R10 plain causal attention on subsequence positions, scale 1/sqrt(d).
-  R11 scatter: a token's output is the mean of the outputs of its selected
-      ancestors (itself included at level 0), levels summed in ascending order.
-  R12 backward: the exact gradient of R3..R11 with the selection held fixed.
+  R11 scatter ("span" mode): a token's output is the mean of the outputs of
+      its selected ancestors (itself included at level 0), levels summed in
+      ascending order.  A coarse entry's output reaches every token of its
+      span, so a token reads up to p**(L-1) - 1 later tokens through its
+      coarsest ancestor: NOT causal.
+  R11c scatter ("causal" mode): the output of entry (l, j) goes to the p**l
+      tokens end(l, j) .. end(l, j) + p**l - 1, i.e. token t receives, per
+      level, the last entry completed at or before t: j = (t+1)//p**l - 1
+      (level 0: the token itself).  Mean over the selected ones; a token with
+      none gets 0.  Every input of out[t] then lies at or before t.
+  R12 backward: the exact gradient of R3..R11 (R11c) with the selection held
+      fixed.
 
 Precision: every tensor step is computed in float64 from its stored inputs and
 rounded once (nearest-even) to the storage type ("fp32", "bf16", or "f64" for
@@ -289,42 +298,72 @@ def attention_backward_cols(qs, ks, vs, dos, lse, D, cols):
 
 # ----------------------------------------------------------------------------
 # stage 6: deterministic scatter back to tokens
-# [TS-es 2.C "Dispersión hacia atrás"], [BG phase 4], [TS-ja 2.C]
+# [TS-es 2.C "Dispersión hacia atrás"], [BG phase 4], [TS-ja 2.C]; the
+# causal reading follows [BG phase 4] (the scatter keeps causality, no token
+# sees the future) and [TS-es 3] item 1 (left-to-right causality preserved)
 
 
-def contributors(pos: np.ndarray, N: int, p: int, L: int) -> np.ndarray:
-    """c_t: number of selected ancestors (levels 0..L-1) of every token."""
+SCATTER_MODES = ("span", "causal")
+
+
+def scatter_entry(t, l: int, p: int, mode: str = "span"):
+    """Index j of the level-l entry whose output token(s) t receive, or -1.
+
+    span (R11): the entry whose span holds t, t // p**l.
+    causal (R11c): the last level-l entry that ends at or before t,
+    (t + 1) // p**l - 1 (its output then feeds the p**l tokens from its end
+    token on)."""
+    if mode == "span":
+        return t // p ** l
+    assert mode == "causal", mode
+    return (t + 1) // p ** l - 1
+
+
+def _feeds(pos, N, p, L, mode):
+    """Per level: (entry index j per token, subsequence position or -1)."""
     bases = level_bases(N, p, L)
     t = np.arange(N)
-    c = np.zeros(N, dtype=np.int64)
+    out = []
     for l in range(L):
-        c += pos[bases[l] + t // p ** l] >= 0
+        j = scatter_entry(t, l, p, mode)
+        r = np.where(j >= 0, pos[bases[l] + np.maximum(j, 0)], -1)
+        out.append((j, r))
+    return out
+
+
+def contributors(pos: np.ndarray, N: int, p: int, L: int, mode: str = "span") -> np.ndarray:
+    """c_t: number of selected entries whose output token t receives (span:
+    its selected ancestors, 1..L of them; causal: 0..L)."""
+    c = np.zeros(N, dtype=np.int64)
+    for _, r in _feeds(pos, N, p, L, mode):
+        c += r >= 0
     return c
 
 
-def ancestors(t: int, pos: np.ndarray, N: int, p: int, L: int):
-    """[(level, subsequence position)] of token t's selected ancestors, level 0 first."""
+def ancestors(t: int, pos: np.ndarray, N: int, p: int, L: int, mode: str = "span"):
+    """[(level, subsequence position)] of the selected entries feeding token t,
+    level 0 first (span: t's selected ancestors)."""
     bases = level_bases(N, p, L)
     out = []
     for l in range(L):
-        r = int(pos[bases[l] + t // p ** l])
+        j = int(scatter_entry(t, l, p, mode))
+        r = int(pos[bases[l] + j]) if j >= 0 else -1
         if r >= 0:
             out.append((l, r))
     return out
 
 
-def scatter(os_: np.ndarray, pos: np.ndarray, N: int, p: int, L: int) -> np.ndarray:
-    """out[t] = mean over t's selected ancestors e of O_sub[pos(e)] (R11)."""
-    bases = level_bases(N, p, L)
-    t = np.arange(N)
+def scatter(os_: np.ndarray, pos: np.ndarray, N: int, p: int, L: int, mode: str = "span") -> np.ndarray:
+    """out[t] = mean over the selected entries e feeding t of O_sub[pos(e)]
+    (R11 / R11c); 0 for a token that no selected entry feeds (causal mode
+    only)."""
     acc = np.zeros((N, os_.shape[1]))
     cnt = np.zeros(N)
-    for l in range(L):
-        r = pos[bases[l] + t // p ** l]
+    for _, r in _feeds(pos, N, p, L, mode):
         hit = r >= 0
         acc[hit] += os_[r[hit]]
         cnt += hit
-    return acc / cnt[:, None]
+    return np.where(cnt[:, None] > 0, acc / np.maximum(cnt, 1)[:, None], 0.0)
 
 
 # ----------------------------------------------------------------------------
@@ -356,9 +395,10 @@ def pooled_rows(x64: np.ndarray, flat: np.ndarray, p: int, L: int, dtype: str) -
 # whole layer, one head
 
 
-def forward_head(q, k, v, p: int, L: int, S: int, dtype: str):
+def forward_head(q, k, v, p: int, L: int, S: int, dtype: str, mode: str = "span"):
     """Forward of one head from stored [N, d] inputs; returns every
-    intermediate the library exposes, each in its storage form."""
+    intermediate the library exposes, each in its storage form.  `mode`
+    selects the scatter reading (R11 "span" or R11c "causal")."""
     N, d = q.shape
     sizes = level_sizes(N, p, L)
     q64, k64, v64 = (to_f64(x, dtype) for x in (q, k, v))
@@ -372,20 +412,20 @@ def forward_head(q, k, v, p: int, L: int, S: int, dtype: str):
     qs, ks, vs = (gather_rows(lv[n], sub_idx, N, p, L) for n in ("q", "k", "v"))
     o, lse = attention(qs, ks, vs)
     os_ = round_to(o, "f64" if dtype == "f64" else "fp32")   # the layer keeps O in float32
-    out = round_to(scatter(to_f64(os_, "fp32"), pos, N, p, L), dtype)
+    out = round_to(scatter(to_f64(os_, "fp32"), pos, N, p, L, mode), dtype)
     return dict(pq=pyr["q"], pk=pyr["k"], pv=pyr["v"], score=score, sel=sel,
                 sub_idx=sub_idx, pos=pos,
                 qs=round_to(qs, dtype), ks=round_to(ks, dtype), vs=round_to(vs, dtype),
-                os=os_, lse=lse.astype(np.float32), out=out, M=sum(sizes))
+                os=os_, lse=lse.astype(np.float32), out=out, M=sum(sizes), mode=mode)
 
 
-def forward_fixed(q64, k64, v64, sub_idx, pos, p: int, L: int):
+def forward_fixed(q64, k64, v64, sub_idx, pos, p: int, L: int, mode: str = "span"):
     """float64 forward with the selection held fixed (for gradient checks)."""
     N = q64.shape[0]
     lv = {n: pyramid(x, p, L) for n, x in (("q", q64), ("k", k64), ("v", v64))}
     qs, ks, vs = (gather_rows(lv[n], sub_idx, N, p, L) for n in ("q", "k", "v"))
     o, _ = attention(qs, ks, vs)
-    return scatter(o, pos, N, p, L)
+    return scatter(o, pos, N, p, L, mode)
 
 
 # ----------------------------------------------------------------------------
@@ -407,16 +447,16 @@ def attention_backward(qs, ks, vs, dos):
     return tau * dS @ ks, tau * dS.T @ qs, dV
 
 
-def scatter_backward(dout, pos, S, N, p, L):
-    """dO_sub[pos(e)] = sum over tokens t of e's span of dout[t] / c_t (R11, R12)."""
-    bases = level_bases(N, p, L)
-    g = dout / contributors(pos, N, p, L)[:, None]
+def scatter_backward(dout, pos, S, N, p, L, mode: str = "span"):
+    """dO_sub[pos(e)] = sum over the tokens t that entry e feeds of
+    dout[t] / c_t (R11: e's span; R11c: the p**l tokens from e's end on),
+    the adjoint of `scatter` (R12)."""
+    c = contributors(pos, N, p, L, mode)
+    g = np.where(c[:, None] > 0, dout / np.maximum(c, 1)[:, None], 0.0)
     dos = np.zeros((S, dout.shape[1]))
-    for l in range(L):
-        span_sums = g.reshape(N // p ** l, p ** l, -1).sum(axis=1)
-        r = pos[bases[l]: bases[l] + N // p ** l]
+    for j, r in _feeds(pos, N, p, L, mode):
         hit = r >= 0
-        dos[r[hit]] = span_sums[hit]
+        np.add.at(dos, r[hit], g[hit])
     return dos
 
 
@@ -439,7 +479,7 @@ def backward_stages(dout, fwd: dict, p: int, L: int, dtype: str) -> dict:
     S = len(sub_idx)
     N = len(dout)
     qs, ks, vs = (to_f64(fwd[n], dtype) for n in ("qs", "ks", "vs"))
-    dos = scatter_backward(to_f64(dout, dtype), pos, S, N, p, L)
+    dos = scatter_backward(to_f64(dout, dtype), pos, S, N, p, L, fwd.get("mode", "span"))
     dqs, dks, dvs = attention_backward(qs, ks, vs, dos)
     dq, dk, dv = (pool_backward(x, pos, N, p, L) for x in (dqs, dks, dvs))
     return dict(dos=dos, dqs=dqs, dks=dks, dvs=dvs, dq=dq, dk=dk, dv=dv)
@@ -455,9 +495,9 @@ def backward_head(dout, fwd: dict, p: int, L: int, dtype: str):
 # batched convenience wrappers over [B, H, N, d]
 
 
-def forward(q, k, v, p, L, S, dtype):
+def forward(q, k, v, p, L, S, dtype, mode="span"):
     B, H = q.shape[:2]
-    return [[forward_head(q[b, h], k[b, h], v[b, h], p, L, S, dtype) for h in range(H)]
+    return [[forward_head(q[b, h], k[b, h], v[b, h], p, L, S, dtype, mode) for h in range(H)]
             for b in range(B)]
 
 

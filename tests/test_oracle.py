@@ -142,6 +142,10 @@ def test_golden_tiny_selection():
     np.testing.assert_array_equal(sub_idx, g["sub_idx"])
     np.testing.assert_array_equal(pos, g["pos"])
     np.testing.assert_array_equal(O.contributors(pos, N, p, L), g["contributors"])
+    np.testing.assert_array_equal(O.contributors(pos, N, p, L, "causal"), g["contributors_causal"])
+    for t, want in enumerate(g["feeders_causal"]):
+        assert [O.level_bases(N, p, L)[l] + int(O.scatter_entry(t, l, p, "causal"))
+                for l, _ in O.ancestors(t, pos, N, p, L, "causal")] == want, t
     v = np.stack([np.arange(N), np.ones(N)], 1).astype(np.float64)
     lv = O.pyramid(v, p, L)
     np.testing.assert_array_equal(lv[1], g["v_level1"])
@@ -308,12 +312,13 @@ def test_forward_bf16_storage_and_shapes():
 
 # ---------------------------------------------------------------- backward
 
-def test_backward_matches_finite_differences():
+@pytest.mark.parametrize("mode", O.SCATTER_MODES)
+def test_backward_matches_finite_differences(mode):
     """Selection held fixed: central differences of sum(out * dout)."""
     r = rng(11)
     N, d, p, L, S = 16, 4, 2, 3, 4 + 5
     q, k, v, dout = (r.standard_normal((N, d)) for _ in range(4))
-    f = O.forward_head(q, k, v, p, L, S, "f64")
+    f = O.forward_head(q, k, v, p, L, S, "f64", mode)
     grads = O.backward_head(dout, f, p, L, "f64")
     h = 1e-6
     for which, g in zip(range(3), grads):
@@ -321,10 +326,96 @@ def test_backward_matches_finite_differences():
             for c in range(d):
                 xs = [q.copy(), k.copy(), v.copy()]
                 xs[which][t, c] += h
-                fp = (O.forward_fixed(*xs, f["sub_idx"], f["pos"], p, L) * dout).sum()
+                fp = (O.forward_fixed(*xs, f["sub_idx"], f["pos"], p, L, mode) * dout).sum()
                 xs[which][t, c] -= 2 * h
-                fm = (O.forward_fixed(*xs, f["sub_idx"], f["pos"], p, L) * dout).sum()
+                fm = (O.forward_fixed(*xs, f["sub_idx"], f["pos"], p, L, mode) * dout).sum()
                 assert abs((fp - fm) / (2 * h) - g[t, c]) < 1e-6 * (1 + abs(g[t, c]))
+
+
+def _dependencies(mode, N, p, L, S, seed, d=4):
+    """dep[t, s]: out[t] changes when token s's q, k or v row changes
+    (selection held fixed).  float64 results that do not depend on token s
+    come out bit-identical, so "changes" is an exact test."""
+    r = rng(seed)
+    q, k, v = (r.standard_normal((N, d)) for _ in range(3))
+    f = O.forward_head(q, k, v, p, L, S, "f64", mode)
+    base = O.forward_fixed(q, k, v, f["sub_idx"], f["pos"], p, L, mode)
+    dep = np.zeros((N, N), bool)
+    for s in range(N):
+        for which in range(3):
+            xs = [q.copy(), k.copy(), v.copy()]
+            xs[which][s] += 1e-3 * r.standard_normal(d)
+            out = O.forward_fixed(*xs, f["sub_idx"], f["pos"], p, L, mode)
+            dep[:, s] |= np.any(out != base, axis=1)
+    return dep, f
+
+
+@pytest.mark.parametrize("N,p,L,S,seed", [(64, 4, 3, 4 + 12, 30), (54, 3, 3, 6 + 9, 31),
+                                          (32, 2, 4, 4 + 20, 32)])
+def test_span_scatter_look_ahead_set(N, p, L, S, seed):
+    """R11 (span broadcast) is not causal: out[t] depends on exactly the later
+    tokens s with t < s <= end of t's coarsest span (the coarsest ancestor is
+    always selected, and every selected ancestor's span lies inside it), and
+    on no other later token."""
+    dep, _ = _dependencies("span", N, p, L, S, seed)
+    P = p ** (L - 1)
+    for t in range(N):
+        E = (t // P + 1) * P - 1
+        later = np.arange(t + 1, N)
+        np.testing.assert_array_equal(dep[t, later], later <= E, err_msg=f"token {t}")
+    # so all but the last token of each coarsest span read the future: 1 - p^-(L-1) of tokens
+    reads_future = [t for t in range(N) if dep[t, t + 1:].any()]
+    assert len(reads_future) == N - N // P
+
+
+@pytest.mark.parametrize("N,p,L,S,seed", [(64, 4, 3, 4 + 12, 30), (54, 3, 3, 6 + 9, 31),
+                                          (32, 2, 4, 4 + 20, 32), (64, 4, 3, 4, 33)])
+def test_causal_scatter_reads_no_later_token(N, p, L, S, seed):
+    """R11c: no out[t] depends on any token s > t ([BG] phase 4: the scatter
+    keeps causality; [TS-es] §3 item 1: left-to-right causality)."""
+    dep, f = _dependencies("causal", N, p, L, S, seed)
+    assert not np.triu(dep, 1).any()
+    # and every token with a contributor depends on something (no dead rows)
+    c = O.contributors(f["pos"], N, p, L, "causal")
+    assert all(dep[t].any() for t in range(N) if c[t] > 0)
+
+
+def test_causal_feeding_windows():
+    """Closed form of R11c: entry (l, j) feeds exactly the tokens
+    end(l, j) .. end(l, j) + p**l - 1 that exist."""
+    N, p, L = 64, 4, 3
+    t = np.arange(N)
+    for l in range(L):
+        j = O.scatter_entry(t, l, p, "causal")
+        for jj in range(-1, N // p ** l):
+            fed = t[j == jj]
+            if jj < 0:
+                np.testing.assert_array_equal(fed, np.arange(p ** l - 1))
+                continue
+            end = (jj + 1) * p ** l - 1
+            np.testing.assert_array_equal(fed, np.arange(end, min(end + p ** l, N)))
+
+
+def test_causal_constant_values_pass_through():
+    """Constant V: a token with contributors outputs that row, one without
+    outputs 0."""
+    r = rng(8)
+    N, d, p, L = 64, 8, 4, 3
+    q, k = r.standard_normal((N, d)), r.standard_normal((N, d))
+    v = np.tile(r.standard_normal((1, d)), (N, 1))
+    f = O.forward_head(q, k, v, p, L, S=4 + 10, dtype="f64", mode="causal")
+    c = O.contributors(f["pos"], N, p, L, "causal")
+    assert (c == 0).any() and (c > 0).any()
+    np.testing.assert_allclose(f["out"][c > 0], v[c > 0], atol=1e-12)
+    assert np.all(f["out"][c == 0] == 0)
+
+
+def test_causal_degenerate_is_dense_causal_attention():
+    r = rng(7)
+    N, d = 64, 16
+    q, k, v = (r.standard_normal((N, d)) for _ in range(3))
+    f = O.forward_head(q, k, v, p=4, L=1, S=N, dtype="f64", mode="causal")
+    np.testing.assert_allclose(f["out"], sdpa64(q, k, v), rtol=1e-12, atol=1e-12)
 
 
 def test_backward_degenerate_matches_torch_autograd():
@@ -340,13 +431,15 @@ def test_backward_degenerate_matches_torch_autograd():
         np.testing.assert_allclose(mine, tt.grad[0, 0].numpy(), rtol=1e-10, atol=1e-10)
 
 
-def test_every_token_gets_gradient():
-    """No holes: every token has a contributor, so every input row gets a
-    gradient path (bitsgeniais post, phase 3)."""
+@pytest.mark.parametrize("mode", O.SCATTER_MODES)
+def test_every_token_gets_gradient(mode):
+    """No holes: every token's coarsest ancestor is selected and feeds at
+    least one token, so every input row gets a gradient path (bitsgeniais
+    post, phase 3)."""
     r = rng(13)
     N, d, p, L = 64, 8, 4, 3
     q, k, v, dout = (r.standard_normal((N, d)) for _ in range(4))
-    f = O.forward_head(q, k, v, p, L, 4 + 3, "f64")
+    f = O.forward_head(q, k, v, p, L, 4 + 3, "f64", mode)
     dq, dk, dv = O.backward_head(dout, f, p, L, "f64")
     assert np.all(np.abs(dv).sum(1) > 0)
 
