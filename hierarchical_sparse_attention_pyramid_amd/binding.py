@@ -16,6 +16,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "liblighthouse.so")
 
 LH_FP32, LH_BF16 = 0, 1
+LH_SCATTER_SPAN, LH_SCATTER_CAUSAL = 0, 1
+SCATTER = {"span": LH_SCATTER_SPAN, "causal": LH_SCATTER_CAUSAL}
 STATUS = {0: "LH_OK", 1: "LH_EINVAL", 2: "LH_EUNSUPPORTED", 3: "LH_EWORKSPACE", 4: "LH_EHIP"}
 DTYPES = {torch.float32: LH_FP32, torch.bfloat16: LH_BF16}
 
@@ -30,7 +32,8 @@ class Shape(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int64), ("H", ctypes.c_int64), ("N", ctypes.c_int64),
                 ("d", ctypes.c_int64), ("p", ctypes.c_int32), ("L", ctypes.c_int32),
                 ("S", ctypes.c_int64), ("dtype", ctypes.c_int32),
-                ("qkv_stride", ctypes.c_int64 * 3), ("out_stride", ctypes.c_int64 * 3)]
+                ("qkv_stride", ctypes.c_int64 * 3), ("out_stride", ctypes.c_int64 * 3),
+                ("scatter", ctypes.c_int32)]
 
 
 class Sizes(ctypes.Structure):
@@ -118,13 +121,15 @@ def _check(status: int):
         raise LighthouseError(status, load_library().lh_last_error().decode())
 
 
-def make_shape(B, H, N, d, p, L, S, dtype, qkv_stride=None, out_stride=None) -> Shape:
+def make_shape(B, H, N, d, p, L, S, dtype, qkv_stride=None, out_stride=None,
+               scatter="span") -> Shape:
     """Shape with optional element strides (b, h, n) of the token tensors:
     qkv_stride for q, k, v, dq, dk, dv; out_stride for out and dout (None =
-    packed [B,H,N,d])."""
+    packed [B,H,N,d]); scatter: "span" or "causal" (or the LH_SCATTER_* value)."""
     if isinstance(dtype, torch.dtype):
         dtype = DTYPES[dtype]
     sh = Shape(B, H, N, d, p, L, S, dtype)
+    sh.scatter = SCATTER.get(scatter, scatter) if isinstance(scatter, str) else scatter
     if qkv_stride is not None:
         sh.qkv_stride = (ctypes.c_int64 * 3)(*qkv_stride)
     if out_stride is not None:
@@ -146,7 +151,8 @@ def with_strides(shape: Shape, qkv_stride=None, out_stride=None) -> Shape:
     """A copy of `shape` with the given token strides (None = keep)."""
     return make_shape(shape.B, shape.H, shape.N, shape.d, shape.p, shape.L, shape.S, shape.dtype,
                       tuple(shape.qkv_stride) if qkv_stride is None else qkv_stride,
-                      tuple(shape.out_stride) if out_stride is None else out_stride)
+                      tuple(shape.out_stride) if out_stride is None else out_stride,
+                      shape.scatter)
 
 
 # ------------------------------------------------------------- the C ABI
@@ -264,8 +270,9 @@ def workspace(nbytes: int, device="cuda") -> torch.Tensor | None:
     return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device) if nbytes else None
 
 
-def forward(q, k, v, p: int, L: int, S: int, out=None, stream=None):
+def forward(q, k, v, p: int, L: int, S: int, out=None, stream=None, scatter="span"):
     """out, buffers, shape for [B,H,N,d] device tensors (fp32 or bf16).
+    scatter: "span" (R11, reads later tokens) or "causal" (R11c).
 
     q, k, v may be strided views sharing one layout (last dimension
     contiguous), e.g. slices of a packed projection; otherwise they are made
@@ -282,7 +289,7 @@ def forward(q, k, v, p: int, L: int, S: int, out=None, stream=None):
     ost = token_strides(out)
     if ost is None:
         raise ValueError("out must be a [B,H,N,d] view with a contiguous last dimension")
-    shape = make_shape(B, H, N, d, p, L, S, q.dtype, st, ost)
+    shape = make_shape(B, H, N, d, p, L, S, q.dtype, st, ost, scatter)
     bufs = LayerBuffers(shape, q.device)
     ws = workspace(bufs.sizes.ws_forward, q.device)
     lh_forward(shape, q, k, v, out, bufs, ws, stream)

@@ -32,8 +32,9 @@ struct PoolBwdArgs {
   void* dos;             // [BH][S][d] (dtype)
   float* sums_out;       // [BH][out_rows][d] or null
   const int32_t* pos;    // [BH][M]
-  int64_t in_rows, out_rows;
+  int64_t in_rows, out_rows;  // virtual rows (see shift)
   int32_t lvl0, lam, chunk;
+  int32_t shift;         // 0: span reading; 1: causal reading (virtual row u = token u - 1)
   Geo g;
 };
 
@@ -43,6 +44,7 @@ struct BcastArgs {
   Lay lout;
   const int32_t* pos;    // [BH][M]
   int32_t mean;          // 1: mean over contributors; 0: weight 1/p^level
+  int32_t shift;         // 0: span reading; 1: causal reading (forward scatter only)
   Geo g;
 };
 

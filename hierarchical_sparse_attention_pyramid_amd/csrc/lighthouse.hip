@@ -26,7 +26,8 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct Stage {
   int lvl0, lam, chunk;
-  int64_t rows_in, rows_out;
+  int64_t rows_in, rows_out;      // forward pooling: rows per head
+  int64_t brows_in, brows_out;    // scatter backward: virtual rows per head
   int out_buf;  // 0 = A, 1 = B, -1 = no f32 sums written
 };
 
@@ -35,6 +36,7 @@ struct Plan {
   lh::Lay tin, tout;  // token tensors: q, k, v, dq, dk, dv / out, dout
   int64_t B, H, BH;
   int dtype;
+  int sh;  // scatter reading: 0 span, 1 causal (virtual token u = t + 1)
   size_t es;
   lh_sizes sz;
   int nstages;
@@ -101,6 +103,8 @@ lh_status make_plan(const lh_shape* s, Plan& P) {
   if (s->B < 1 || s->H < 1 || s->N < 1 || s->d < 1)
     return fail(LH_EINVAL, "B, H, N and d must be positive");
   if (s->dtype != LH_FP32 && s->dtype != LH_BF16) return fail(LH_EINVAL, "unknown dtype");
+  if (s->scatter != LH_SCATTER_SPAN && s->scatter != LH_SCATTER_CAUSAL)
+    return fail(LH_EINVAL, "unknown scatter reading");
   if (s->p < 2) return fail(LH_EINVAL, "pooling factor p must be >= 2");
   if (s->p > 64) return fail(LH_EUNSUPPORTED, "pooling factor p > 64 is not supported");
   if (s->L < 1) return fail(LH_EINVAL, "L must be >= 1");
@@ -160,12 +164,16 @@ lh_status make_plan(const lh_shape* s, Plan& P) {
   P.BH = BH;
   P.dtype = s->dtype;
   P.es = s->dtype == LH_BF16 ? 2 : 4;
+  // with one level both readings feed token t from entry t alone: run the span form
+  P.sh = s->scatter == LH_SCATTER_CAUSAL && s->L > 1 ? 1 : 0;
+  // the causal scatter backward pools N + p^(L-1) virtual rows (see pyramid.hip)
+  const int64_t nvb = s->N + (P.sh ? pw : 0);
 
   // pooling passes
   P.nstages = 0;
   P.sums_rows[0] = P.sums_rows[1] = 0;
   if (s->L == 1) {
-    P.st[P.nstages++] = Stage{0, 0, 64, s->N, s->N, -1};
+    P.st[P.nstages++] = Stage{0, 0, 64, s->N, s->N, nvb, nvb, -1};
   } else {
     const int lm = lam_max(s->p);
     int lvl = 0;
@@ -177,13 +185,15 @@ lh_status make_plan(const lh_shape* s, Plan& P) {
       // rows, so they take one span per row group to keep the GPU busy
       const int64_t rep = lvl == 0 ? std::max<int64_t>(1, LH_POOL_TOKCHUNK / plam) : 1;
       const int64_t rows_in = s->N / g.pw[lvl];
-      Stage t{lvl, lam, (int)(plam * rep), rows_in, rows_in / plam, -1};
+      const int64_t brows_in = nvb / g.pw[lvl];
+      Stage t{lvl, lam, (int)(plam * rep), rows_in, rows_in / plam, brows_in, brows_in / plam, -1};
       P.st[P.nstages++] = t;
       lvl += lam;
     }
     for (int k = 0; k + 1 < P.nstages; ++k) {
       P.st[k].out_buf = k % 2;
-      P.sums_rows[k % 2] = std::max<size_t>(P.sums_rows[k % 2], (size_t)P.st[k].rows_out);
+      P.sums_rows[k % 2] = std::max<size_t>(
+          P.sums_rows[k % 2], (size_t)std::max(P.st[k].rows_out, P.st[k].brows_out));
     }
   }
 
@@ -398,6 +408,7 @@ lh_status lh_scatter(const lh_shape* shape, const float* os, const int32_t* pos,
   a.out[0] = out;
   a.pos = pos;
   a.mean = 1;
+  a.shift = P.sh;
   a.lout = P.tout;
   a.g = P.g;
   LH_HIP(lh::launch_bcast(a, P.dtype, 1, P.BH, static_cast<hipStream_t>(stream)),
@@ -453,6 +464,7 @@ static lh_status run_forward(const Plan& P, const void* q, const void* k, const 
   a.out[0] = out;
   a.pos = b->pos;
   a.mean = 1;
+  a.shift = P.sh;
   a.lout = P.tout;
   a.g = P.g;
   LH_HIP(lh::launch_bcast(a, P.dtype, 1, P.BH, st), "scatter");
@@ -479,12 +491,13 @@ static lh_status run_scatter_bwd(const Plan& P, const void* dout, const int32_t*
     a.dos = dos;
     a.sums_out = t.out_buf >= 0 ? sums_ptr(P, ws, t.out_buf, 0) : nullptr;
     a.pos = pos;
-    a.lin = s == 0 ? P.tout : lh::packed_lay(P.H, t.rows_in, P.g.d);
-    a.in_rows = t.rows_in;
-    a.out_rows = t.rows_out;
+    a.lin = s == 0 ? P.tout : lh::packed_lay(P.H, t.brows_in, P.g.d);
+    a.in_rows = t.brows_in;
+    a.out_rows = t.brows_out;
     a.lvl0 = t.lvl0;
     a.lam = t.lam;
     a.chunk = t.chunk;
+    a.shift = P.sh;
     a.g = P.g;
     LH_HIP(lh::launch_pool_bwd(a, P.dtype, P.BH, s == 0, st), "scatter_backward");
   }
@@ -550,6 +563,7 @@ lh_status lh_gather_backward(const lh_shape* shape, const float* dqs, const floa
   a.out[2] = dv;
   a.pos = pos;
   a.mean = 0;
+  a.shift = 0;  // the pooling adjoint: spans, in either scatter reading
   a.lout = P.tin;
   a.g = P.g;
   LH_HIP(lh::launch_bcast(a, P.dtype, 3, P.BH, static_cast<hipStream_t>(stream)),
@@ -605,6 +619,7 @@ static lh_status run_backward(const Plan& P, const void* dout, const lh_buffers*
   a.out[2] = dv;
   a.pos = b->pos;
   a.mean = 0;
+  a.shift = 0;  // the pooling adjoint: spans, in either scatter reading
   a.lout = P.tin;
   a.g = P.g;
   LH_HIP(lh::launch_bcast(a, P.dtype, 3, P.BH, st), "gather_backward");

@@ -206,9 +206,13 @@ __global__ __launch_bounds__(256) void pool_fwd_kernel(PoolFwdArgs a, int do_poo
   }
 }
 
-// Scatter backward: dos[pos(e)] = sum over tokens t of e's span of
-// dout[t] / c_t.  Same row-group walk as the forward; only selected entries
-// are written.  On the token pass, c_t (the number of selected ancestors of
+// Scatter backward: dos[pos(e)] = sum over the tokens t that entry e feeds
+// of dout[t] / c_t (0 for a token that nothing feeds).  Same row-group walk
+// as the forward; only selected entries are written.  The causal reading
+// (shift = 1: entry (l, j) feeds the p^l tokens from its end token on) is
+// the span reduction over virtual rows u = t + 1, with positions looked up
+// as vpos(l, J) = pos(l, J - 1) and the rows padded with zeros to
+// N + p^(L-1), so that the windows of every level's last entry complete.  On the token pass, c_t (the number of selected ancestors of
 // t) comes from an ancestor walk that keeps per-level counts.  The positions
 // the workgroup needs (its rows' own, the levels it writes and, on the token
 // pass, every ancestor level) are first staged in LDS in one coalesced
@@ -226,6 +230,12 @@ __global__ __launch_bounds__(256) void pool_bwd_kernel(PoolBwdArgs a) {
   const int64_t nchunks = (a.in_rows + a.chunk - 1) / a.chunk;
   const int64_t c = (int64_t)blockIdx.x * rgs + rg;
   const int32_t* pos = a.pos + bh * g.M;
+  const int sh = a.shift;
+  // position of virtual entry j of level l (-1: outside the level or not selected)
+  auto vpos = [&](int l, int32_t j) {
+    const int32_t jj = j - sh;
+    return jj >= 0 && jj < g.nlev[l] ? pos[g.base[l] + jj] : -1;
+  };
 
   // ---- stage positions: rows [B0, B0 + BT) of level lvl0 (token pass), then
   // the entries of every level above lvl0 that these rows belong to
@@ -235,7 +245,7 @@ __global__ __launch_bounds__(256) void pool_bwd_kernel(PoolBwdArgs a) {
   const int64_t BT = min((int64_t)rgs * a.chunk, a.in_rows - B0);
   int off = 0;
   if (FIRST) {
-    for (int i = threadIdx.x; i < BT; i += 256) sp[i] = pos[B0 + i];
+    for (int i = threadIdx.x; i < BT; i += 256) sp[i] = vpos(0, (int32_t)(B0 + i));
     off = (int)BT;
   }
   const int ltop = FIRST ? g.L : min(g.L, a.lvl0 + a.lam + 1);  // levels whose positions are read
@@ -247,7 +257,7 @@ __global__ __launch_bounds__(256) void pool_bwd_kernel(PoolBwdArgs a) {
       soff[l] = off;
       sjlo[l] = jlo;
     }
-    for (int i = threadIdx.x; i <= jhi - jlo; i += 256) sp[off + i] = pos[g.base[l] + jlo + i];
+    for (int i = threadIdx.x; i <= jhi - jlo; i += 256) sp[off + i] = vpos(l, jlo + i);
     off += jhi - jlo + 1;
   }
   __syncthreads();
@@ -286,8 +296,19 @@ __global__ __launch_bounds__(256) void pool_bwd_kernel(PoolBwdArgs a) {
 #pragma unroll
     for (int u = 0; u < kRowsInFlight; ++u) {
       const int64_t row = r0 + min(rb + u, nrows - 1);
-      Row8<Tin>::template load<kStream>(in + row * a.lin.sn, xs[u]);
-      if constexpr (FIRST) pt[u] = sp[row - B0];
+      if constexpr (FIRST) {
+        // token row of virtual row `row`: zeros before the first token and in the padding
+        const int64_t t = row - sh;
+        if (t >= 0 && t < g.N) {
+          Row8<Tin>::template load<kStream>(in + t * a.lin.sn, xs[u]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) xs[u][e] = 0.f;
+        }
+        pt[u] = sp[row - B0];
+      } else {
+        Row8<Tin>::template load<kStream>(in + row * a.lin.sn, xs[u]);
+      }
     }
 #pragma unroll
     for (int u = 0; u < kRowsInFlight; ++u) {
@@ -304,7 +325,7 @@ __global__ __launch_bounds__(256) void pool_bwd_kernel(PoolBwdArgs a) {
           walk.advance((int32_t)row, posf, nullptr, g, true, lane);
           ct += walk.cnt[1];
         }
-        const float rc = 1.0f / static_cast<float>(ct);
+        const float rc = ct > 0 ? 1.0f / static_cast<float>(ct) : 0.0f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) xs[u][e] *= rc;
         if (pt[u] >= 0) Row8<Tout>::store(dos + (int64_t)pt[u] * d, xs[u]);

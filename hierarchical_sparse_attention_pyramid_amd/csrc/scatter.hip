@@ -7,6 +7,15 @@
 //    of dXs[pos(e)] / p^level(e) (the adjoint of "copy entry e into the
 //    subsequence" composed with "entry e = mean of its p^level tokens").
 //
+// The causal reading of the forward scatter (bitsgeniais phase 4: no token
+// sees the future) sends entry (l, j)'s output to the p^l tokens from its end
+// token on, so token t receives, per level, entry (t + 1) / p^l - 1.  That is
+// the span rule applied to the virtual token u = t + 1 with every entry index
+// lowered by one, which is how both kernels run it: they walk u in
+// [0, N + shift), look positions up through vpos(l, J) = pos(l, J - shift)
+// (-1 outside the level) and write token u - shift.  A token that no selected
+// entry feeds (causal only) gets zeros.
+//
 // Sources are float32 rows (the attention output, or the float32 gradients
 // of the subsequence); outputs are in the storage type.
 // Both are pulls: every output row is written by exactly one row group, so
@@ -74,14 +83,20 @@ __global__ __launch_bounds__(256) void bcast_kernel(BcastArgs a) {
     src[i] = a.src[i] + bh * (int64_t)g.S * g.d;
     out[i] = static_cast<Tout*>(a.out[i]) + a.lout.head(bh) + kE * lane;
   }
+  const int sh = a.shift;
+  const int32_t nv = g.N + sh;  // virtual tokens u = t + shift
+  auto vpos = [&](int l, int32_t j) {
+    const int32_t jj = j - sh;
+    return jj >= 0 && jj < g.nlev[l] ? pos[g.base[l] + jj] : -1;
+  };
   const int32_t t0 = ((int32_t)blockIdx.x * rgs + rg) * kTokPerGroup;
-  if (t0 >= g.N) return;  // no block-wide barrier in this kernel
-  const int32_t t1 = min(t0 + kTokPerGroup, g.N);
+  if (t0 >= nv) return;  // no block-wide barrier in this kernel
+  const int32_t t1 = min(t0 + kTokPerGroup, nv);
   AncestorWalk<NT, kE> w;
   for (int32_t t = t0; t < t1; t += kU) {
     int32_t r0[kU];
 #pragma unroll
-    for (int u = 0; u < kU; ++u) r0[u] = t + u < t1 ? pos[t + u] : -1;
+    for (int u = 0; u < kU; ++u) r0[u] = t + u < t1 ? vpos(0, t + u) : -1;
     float v0[kU][NT][kE];
 #pragma unroll
     for (int u = 0; u < kU; ++u)
@@ -95,15 +110,16 @@ __global__ __launch_bounds__(256) void bcast_kernel(BcastArgs a) {
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       if (t + u >= t1) break;
-      w.advance(t + u, [&](int l, int32_t j) { return pos[g.base[l] + j]; }, src, g, mean, lane);
+      w.advance(t + u, vpos, src, g, mean, lane);
+      if (t + u < sh) continue;  // virtual token 0 of the causal reading: no output row
       const int c = w.cnt[1] + (r0[u] >= 0 ? 1 : 0);
-      const float rc = mean ? 1.0f / static_cast<float>(c) : 1.0f;
+      const float rc = mean ? (c > 0 ? 1.0f / static_cast<float>(c) : 0.0f) : 1.0f;
 #pragma unroll
       for (int i = 0; i < NT; ++i) {
         float o[kE];
 #pragma unroll
         for (int e = 0; e < kE; ++e) o[e] = (w.A[1][i][e] + v0[u][i][e]) * rc;
-        Out4<Tout>::store(out[i] + (int64_t)(t + u) * a.lout.sn, o);
+        Out4<Tout>::store(out[i] + (int64_t)(t + u - sh) * a.lout.sn, o);
       }
     }
   }
@@ -148,25 +164,31 @@ __global__ __launch_bounds__(256) void bcast_fast(BcastArgs a) {
   const int32_t B0 = (int32_t)blockIdx.x * BT;
   const int32_t* pos = a.pos + bh * g.M;
   const int lg = g.log2p;
+  const int sh = a.shift;
+  const int32_t nv = g.N + sh;  // virtual tokens u = t + shift
   __shared__ int32_t sp[kPosCache];
   __shared__ int32_t soff[kMaxLevels];  // start of level l's run in sp
 
-  // ---- stage positions: tokens [B0, B0 + BT), then each level's ancestors
-  for (int i = threadIdx.x; i < BT; i += 256) sp[i] = B0 + i < g.N ? pos[B0 + i] : -1;
+  // ---- stage positions vpos: virtual tokens [B0, B0 + BT), then each
+  // level's ancestors of them
+  for (int i = threadIdx.x; i < BT; i += 256) {
+    const int32_t t = B0 + i - sh;
+    sp[i] = t >= 0 && t < g.N ? pos[t] : -1;
+  }
   const int lbt = __builtin_ctz(BT);  // BT is a power of two (64 tokens x 8 or 16 row groups)
   int off = BT;
   for (int l = 1; l < g.L; ++l) {
     const int n = lg * l >= lbt ? 1 : BT >> (lg * l);  // ancestors of the block: max(1, BT / p^l)
-    const int32_t jlo = B0 >> (lg * l);
+    const int32_t jlo = (B0 >> (lg * l)) - sh;
     if (threadIdx.x == 0) soff[l] = off;
     for (int i = threadIdx.x; i < n; i += 256)
-      sp[off + i] = jlo + i < g.nlev[l] ? pos[g.base[l] + jlo + i] : -1;
+      sp[off + i] = jlo + i >= 0 && jlo + i < g.nlev[l] ? pos[g.base[l] + jlo + i] : -1;
     off += n;
   }
   __syncthreads();
   const int32_t t0 = B0 + rg * kFastTok;
-  if (t0 >= g.N) return;  // no barrier below
-  const int32_t t1 = min(t0 + kFastTok, g.N);
+  if (t0 >= nv) return;  // no barrier below
+  const int32_t t1 = min(t0 + kFastTok, nv);
 
   const float* src = a.src[z] + bh * (int64_t)g.S * g.d + kE * lane;
   Tout* out = static_cast<Tout*>(a.out[z]) + a.lout.head(bh) + kE * lane;
@@ -274,11 +296,13 @@ __global__ __launch_bounds__(256) void bcast_fast(BcastArgs a) {
     for (int u = 0; u < kFastU; ++u) {
       const int32_t t = c + u;
       if (t >= t1) break;
-      const float rc = mean ? 1.0f / static_cast<float>(C[0] + b.s0[u]) : 1.0f;
+      if (t < sh) continue;  // virtual token 0 of the causal reading: no output row
+      const int cnt = C[0] + b.s0[u];
+      const float rc = mean ? (cnt > 0 ? 1.0f / static_cast<float>(cnt) : 0.0f) : 1.0f;
       float o[kE];
 #pragma unroll
       for (int e = 0; e < kE; ++e) o[e] = (A[0][e] + b.r0[u][e]) * rc;
-      Out4<Tout>::store(out + (int64_t)t * a.lout.sn, o);
+      Out4<Tout>::store(out + (int64_t)(t - sh) * a.lout.sn, o);
     }
   };
   if (nin == 0) {  // A[0] must be the outer sum
@@ -305,15 +329,16 @@ __global__ __launch_bounds__(256) void bcast_fast(BcastArgs a) {
 
 hipError_t launch_bcast(const BcastArgs& a, int dtype, int ntensors, int64_t BH, hipStream_t st) {
   const int rgs = 256 / (a.g.d / kE);
+  const int64_t nv = (int64_t)a.g.N + a.shift;  // virtual tokens
   if (LH_BC_FAST && a.g.log2p >= 2) {
     const int64_t bt = (int64_t)rgs * kFastTok;
-    const dim3 grid((unsigned)((a.g.N + bt - 1) / bt), (unsigned)BH, (unsigned)ntensors);
+    const dim3 grid((unsigned)((nv + bt - 1) / bt), (unsigned)BH, (unsigned)ntensors);
     if (dtype == 1) bcast_fast<__bf16><<<grid, 256, 0, st>>>(a);
     else bcast_fast<float><<<grid, 256, 0, st>>>(a);
     return hipGetLastError();
   }
   const int64_t per_block = (int64_t)rgs * kTokPerGroup;
-  const dim3 grid((unsigned)((a.g.N + per_block - 1) / per_block), (unsigned)BH);
+  const dim3 grid((unsigned)((nv + per_block - 1) / per_block), (unsigned)BH);
   if (dtype == 1) {
     if (ntensors == 3) bcast_kernel<__bf16, 3><<<grid, 256, 0, st>>>(a);
     else bcast_kernel<__bf16, 1><<<grid, 256, 0, st>>>(a);

@@ -65,6 +65,23 @@ typedef enum {
 
 typedef enum { LH_FP32 = 0, LH_BF16 = 1 } lh_dtype;
 
+/* Scatter reading (how subsequence outputs go back to tokens, bitsgeniais
+ * phase 4; gist.science technical summary §2.C and §3 item 1).
+ *  LH_SCATTER_SPAN (0, the default): token t receives the outputs of its
+ *    selected ancestors, the entries whose span holds t.  NOT causal: every
+ *    token except the last of its coarsest span (1 - p^-(L-1) of all tokens)
+ *    reads later tokens, up to p^(L-1) - 1 of them, through its coarsest
+ *    ancestor (whose pooled q, k, v include them).  Not a drop-in for causal
+ *    attention in language-model training, where it lets a position see the
+ *    tokens it is to predict.
+ *  LH_SCATTER_CAUSAL (1): entry (l, j) feeds the p^l tokens from its end
+ *    token (j+1)*p^l - 1 on, so token t receives, per level, the entry
+ *    (t+1)/p^l - 1 (integer division), the last one completed at or before t
+ *    (level 0: t itself).  out[t] depends on tokens <= t only.  Tokens that
+ *    no selected entry feeds (only possible for t < p^(L-1) - 1) get 0.
+ * Both take the mean over the entries that feed the token. */
+typedef enum { LH_SCATTER_SPAN = 0, LH_SCATTER_CAUSAL = 1 } lh_scatter_mode;
+
 /* Problem shape.  p = pooling factor, L = number of pyramid levels (level 0 =
  * tokens), S = subsequence length.  L = 1 means S = N and the layer is plain
  * dense causal attention.
@@ -83,7 +100,11 @@ typedef enum { LH_FP32 = 0, LH_BF16 = 1 } lh_dtype;
  * bytes, and no two rows overlap (LH_EINVAL if not); the stride of a
  * dimension of extent 1 is ignored.  Tensor pointers must be 16-byte aligned.  Every other
  * tensor of the API (pyramid, scores, maps, subsequence tensors) is packed.
- * Zero-initialising the struct keeps the packed layout. */
+ * Zero-initialising the struct keeps the packed layout and the span scatter.
+ *
+ * scatter: lh_scatter_mode (LH_EINVAL for other values); it changes
+ * lh_scatter, lh_scatter_backward and the fused calls, and the scatter
+ * backward's workspace size. */
 typedef struct {
   int64_t B, H, N, d;
   int32_t p, L;
@@ -91,6 +112,7 @@ typedef struct {
   int32_t dtype; /* lh_dtype */
   int64_t qkv_stride[3];
   int64_t out_stride[3];
+  int32_t scatter; /* lh_scatter_mode */
 } lh_shape;
 
 /* Derived sizes (per (b,h) counts; byte sizes are for all B*H heads). */
@@ -178,22 +200,27 @@ lh_status lh_attention(const lh_shape *shape, const void *qs, const void *ks, co
                        float *os, float *lse, void *stream);
 
 /* a6. Deterministic scatter back to tokens (technical summary §2.C;
- * bitsgeniais phase 4): out[t] = mean over t's selected ancestors e (levels
- * 0..L-1, summed in a fixed order) of os[pos(e)].
+ * bitsgeniais phase 4): out[t] = mean over the selected entries e that feed
+ * token t (levels 0..L-1, summed in a fixed order) of os[pos(e)]; 0 if none.
+ * Which entries feed t is shape->scatter's reading: t's ancestors
+ * (LH_SCATTER_SPAN; reads later tokens, see lh_scatter_mode) or the last
+ * completed entry of each level (LH_SCATTER_CAUSAL).
  * os: float32 [B,H,S,d]; pos: [B,H,M]; out: [B,H,N,d] dtype. */
 lh_status lh_scatter(const lh_shape *shape, const float *os, const int32_t *pos, void *out,
                      void *stream);
 
 /* a1..a6 in one call.  bufs: every field required; out: [B,H,N,d].
- * ws: ws_forward bytes. */
+ * ws: ws_forward bytes.  Causal in the tokens only with
+ * shape->scatter = LH_SCATTER_CAUSAL (see lh_scatter_mode). */
 lh_status lh_forward(const lh_shape *shape, const void *q, const void *k, const void *v,
                      void *out, const lh_buffers *bufs, void *ws, size_t ws_bytes,
                      void *stream);
 
 /* a7. Backward of the scatter (technical summary §2.B: gradients flow through
  * scatter, attention and gather; selection gets none):
- * dos[pos(e)] = sum over tokens t of e's span of dout[t] / c_t, c_t = number
- * of selected ancestors of t.  Rows of dos for positions are all written.
+ * dos[pos(e)] = sum over the tokens t that e feeds of dout[t] / c_t, c_t =
+ * number of selected entries feeding t (tokens with c_t = 0 add nothing);
+ * "feeds" as in lh_scatter for shape->scatter.  Every row of dos is written.
  * dout: [B,H,N,d] dtype; dos: [B,H,S,d] dtype.  ws: ws_scatter_backward. */
 lh_status lh_scatter_backward(const lh_shape *shape, const void *dout, const int32_t *pos,
                               void *dos, void *ws, size_t ws_bytes, void *stream);

@@ -6,7 +6,9 @@ The oracle recomputes sampled parts one by one from the synthetic inputs:
     bit-exact;
   * pooled rows at sampled entries and every gathered subsequence row;
   * attention output and lse at sampled query rows;
-  * layer output at sampled tokens (mean over their ancestors' rows);
+  * layer output at sampled tokens (mean over the rows that feed them: their
+    ancestors, or with the causal scatter the last completed entry of each
+    level);
   * gradients at sampled tokens: the oracle's exact lse and rowsum(dO*O) for
     every row, then dQ at the ancestors' rows and dK, dV at their columns.
 Float bars as elsewhere (bf16: max|g-r| / max|r| <= 2e-2 over the sample;
@@ -43,8 +45,15 @@ def to_dev(a, dtype):
     return torch.from_numpy(a).cuda()
 
 
-@pytest.mark.parametrize("name", WORKLOADS)
-def test_full_size(name, gpu_lib):
+# the causal scatter reading at full size: the headline workload (fast
+# scatter kernels), the small fp32 workload and the p = 2 operating point
+# (generic ancestor-walk kernels)
+CAUSAL = ["train_n98k_bf16", "fwd_n4k_fp32", "op_n98k_p2_bf16"]
+CASES = [(n, "span") for n in WORKLOADS] + [(n, "causal") for n in CAUSAL]
+
+
+@pytest.mark.parametrize("name,mode", CASES, ids=[f"{n}-{m}" for n, m in CASES])
+def test_full_size(name, mode, gpu_lib):
     from hierarchical_sparse_attention_pyramid_amd import binding as lb
     cfg = synth.CONFIGS[name]
     B, H, N, d, p, L, S, dt = cfg.B, cfg.H, cfg.N, cfg.d, cfg.p, cfg.L, cfg.S, cfg.dtype
@@ -52,8 +61,9 @@ def test_full_size(name, gpu_lib):
     names = ("q", "k", "v", "dout") if cfg.backward else ("q", "k", "v")
     host = synth.make_inputs(cfg, tensors=names)
     dev = {n: to_dev(host[n], dt) for n in names}
-    print(f"[gpu-fullsize] {name}: GPU forward{'+backward' if cfg.backward else ''}", flush=True)
-    out, bufs, shape = lb.forward(dev["q"], dev["k"], dev["v"], p, L, S)
+    print(f"[gpu-fullsize] {name} ({mode} scatter): GPU forward{'+backward' if cfg.backward else ''}",
+          flush=True)
+    out, bufs, shape = lb.forward(dev["q"], dev["k"], dev["v"], p, L, S, scatter=mode)
     if cfg.backward:
         dq, dk, dv = lb.backward(shape, dev["dout"], bufs)
     torch.cuda.synchronize()
@@ -79,25 +89,29 @@ def test_full_size(name, gpu_lib):
         for n, t in (("q", bufs.qs), ("k", bufs.ks), ("v", bufs.vs)):
             check_close(to_f64(t[b, h]), orow[n], dt, f"{n}s")
         # sampled tokens and the subsequence rows they need
-        toks = [0, N - 1] + rng.choice(N, 40, replace=False).tolist()
+        P = p ** (L - 1)  # tokens before P - 1 may have no causal feeder
+        toks = [0, 1, 2, max(0, P - 2), P - 1, N - 1] + rng.choice(N, 40, replace=False).tolist()
         if cfg.planted:
             toks += synth.planted_positions(cfg.seed, N)[:8].tolist()
         toks = sorted(set(toks))
-        anc = {t: O.ancestors(t, pos, N, p, L) for t in toks}
-        need = sorted({r for t in toks for _, r in anc[t]})
+        feed = {t: O.ancestors(t, pos, N, p, L, mode) for t in toks}  # entries out[t] reads
+        anc = {t: O.ancestors(t, pos, N, p, L) for t in toks}          # entries pooling t
+        need = sorted({r for t in toks for _, r in anc[t] + feed[t]})
         rows = sorted(set(need) | {0, S - 1} | set(rng.choice(S, 24, replace=False).tolist()))
         o_rows, lse_rows = O.attention_rows(orow["q"], orow["k"], orow["v"], rows)
         idx = torch.tensor(rows).cuda()
         check_close(to_f64(bufs.os[b, h][idx]), o_rows, dt, "os rows")
         check_close(to_f64(bufs.lse[b, h][idx]), lse_rows, dt, "lse rows")
         o_of = dict(zip(rows, o_rows))
-        ref_out = np.stack([np.mean([o_of[r] for _, r in anc[t]], axis=0) for t in toks])
+        d_ = orow["q"].shape[1]
+        ref_out = np.stack([np.mean([o_of[r] for _, r in feed[t]], axis=0) if feed[t]
+                            else np.zeros(d_) for t in toks])
         tix = torch.tensor(toks).cuda()
         check_close(to_f64(out[b, h][tix]), ref_out, dt, "out tokens")
         if not cfg.backward:
             continue
         print(f"[gpu-fullsize] {name}: oracle backward on head ({b},{h})", flush=True)
-        dos = O.scatter_backward(x64["dout"], pos, S, N, p, L)
+        dos = O.scatter_backward(x64["dout"], pos, S, N, p, L, mode)
         O_all, lse_all = O.attention_all_rows(orow["q"], orow["k"], orow["v"])
         D = (dos * O_all).sum(axis=1)
         dqs = O.attention_backward_rows(orow["q"], orow["k"], orow["v"], dos, lse_all, D, need)
