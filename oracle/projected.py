@@ -33,16 +33,18 @@ def _heads(a: np.ndarray, H: int) -> list:
     return [a[:, h * d:(h + 1) * d] for h in range(H)]
 
 
-def projected_forward(x, wq, wk, wv, wo, H: int, p: int, L: int, S: int, dtype: str):
+def projected_forward(x, wq, wk, wv, wo, H: int, p: int, L: int, S: int, dtype: str,
+                      mode: str = "span"):
     """One batch element: x [N, D], wq/wk/wv [H*d, D], wo [D, H*d], all stored
-    in `dtype`.  Returns (y stored, cache for the backward)."""
+    in `dtype`; `mode` is the layer's scatter reading ("span" or "causal").
+    Returns (y stored, cache for the backward)."""
     x64, wq64, wk64, wv64, wo64 = (O.to_f64(a, dtype) for a in (x, wq, wk, wv, wo))
     q, k, v = (O.round_to(x64 @ w.T, dtype) for w in (wq64, wk64, wv64))
-    fwds = [O.forward_head(qh, kh, vh, p, L, S, dtype)
+    fwds = [O.forward_head(qh, kh, vh, p, L, S, dtype, mode)
             for qh, kh, vh in zip(_heads(q, H), _heads(k, H), _heads(v, H))]
     o = np.concatenate([O.to_f64(f["out"], dtype) for f in fwds], axis=1)
     y = O.round_to(o @ wo64.T, dtype)
-    cache = dict(x64=x64, w64=(wq64, wk64, wv64, wo64), o=o, fwds=fwds, H=H, p=p, L=L)
+    cache = dict(x64=x64, w64=(wq64, wk64, wv64, wo64), o=o, fwds=fwds, H=H, p=p, L=L, mode=mode)
     return y, cache
 
 
@@ -62,11 +64,11 @@ def projected_backward(dy, cache: dict, dtype: str):
     return tuple(O.round_to(a, dtype) for a in (dx, dwq, dwk, dwv, dwo))
 
 
-def projected_forward_fixed(x, wq, wk, wv, wo, fwds, H: int, p: int, L: int):
+def projected_forward_fixed(x, wq, wk, wv, wo, fwds, H: int, p: int, L: int, mode: str = "span"):
     """float64 block output with every head's selection held fixed (the
     selections of `fwds`), for gradient checks."""
     q, k, v = (x @ w.T for w in (wq, wk, wv))
-    o = np.concatenate([O.forward_fixed(qh, kh, vh, f["sub_idx"], f["pos"], p, L)
+    o = np.concatenate([O.forward_fixed(qh, kh, vh, f["sub_idx"], f["pos"], p, L, mode)
                         for qh, kh, vh, f in zip(_heads(q, H), _heads(k, H), _heads(v, H), fwds)],
                        axis=1)
     return o @ wo.T

@@ -15,12 +15,15 @@ from tests.helpers import check_close, to_f64
 pytestmark = pytest.mark.gpu
 
 CASES = [
-    # name, N, D, H, d, p, L, S, dtype, B
-    ("block_bf16", 2048, 256, 4, 64, 4, 3, 300, "bf16", 1),
-    ("block_d128_bf16", 1024, 256, 2, 128, 4, 4, 200, "bf16", 1),
-    ("block_fp32", 256, 128, 2, 64, 4, 3, 48, "fp32", 1),
+    # name, N, D, H, d, p, L, S, dtype, B, scatter reading
+    ("block_bf16", 2048, 256, 4, 64, 4, 3, 300, "bf16", 1, "span"),
+    ("block_d128_bf16", 1024, 256, 2, 128, 4, 4, 200, "bf16", 1, "span"),
+    ("block_fp32", 256, 128, 2, 64, 4, 3, 48, "fp32", 1, "span"),
     # two batch elements (packed projections with a batch stride), model width != H*d
-    ("block_b2_D320_bf16", 1296, 320, 3, 64, 6, 3, 250, "bf16", 2),
+    ("block_b2_D320_bf16", 1296, 320, 3, 64, 6, 3, 250, "bf16", 2, "span"),
+    # the module's default, causal scatter
+    ("block_causal_bf16", 2048, 256, 4, 64, 4, 3, 300, "bf16", 1, "causal"),
+    ("block_causal_b2_fp32", 648, 192, 3, 64, 6, 3, 60, "fp32", 2, "causal"),
 ]
 
 
@@ -33,7 +36,7 @@ def dev(a, dtype):
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
 def test_block_matches_oracle(case, gpu_lib):
     from hierarchical_sparse_attention_pyramid_amd.layer import LighthouseAttention
-    name, N, D, H, d, p, L, S, dt, B = case
+    name, N, D, H, d, p, L, S, dt, B, mode = case
     print(f"[gpu-block] {name}: B={B} N={N} D={D} H={H} d={d} p={p} L={L} S={S} {dt}", flush=True)
     seed = 500 + 10 * [c[0] for c in CASES].index(name)
     xs = [synth.block_tensor(seed + 7 * b, (N, D), dt) for b in range(B)]
@@ -42,7 +45,7 @@ def test_block_matches_oracle(case, gpu_lib):
     dys = [synth.block_tensor(seed + 5 + 7 * b, (N, D), dt) for b in range(B)]
 
     tdt = torch.bfloat16 if dt == "bf16" else torch.float32
-    m = LighthouseAttention(D, H, d, p, L, S, dtype=tdt)
+    m = LighthouseAttention(D, H, d, p, L, S, dtype=tdt, scatter=mode)
     with torch.no_grad():
         for prm, a in zip((m.wq, m.wk, m.wv, m.wo), (*ws, wo)):
             prm.copy_(dev(a, dt))
@@ -54,7 +57,7 @@ def test_block_matches_oracle(case, gpu_lib):
     # per batch element: output and dx; weight gradients sum over the batch
     gw = [0.0] * 4
     for b in range(B):
-        yr, cache = P.projected_forward(xs[b], *ws, wo, H, p, L, S, dt)
+        yr, cache = P.projected_forward(xs[b], *ws, wo, H, p, L, S, dt, mode)
         gr = P.projected_backward(dys[b], cache, dt)
         check_close(to_f64(y[b]), O.to_f64(yr, dt), dt, f"block output [{b}]")
         check_close(to_f64(xt.grad[b]), O.to_f64(gr[0], dt), dt, f"dx [{b}]")

@@ -3,6 +3,7 @@ its input and output projections."""
 from __future__ import annotations
 
 import numpy as np
+import pytest
 import torch
 
 from oracle import lighthouse as O
@@ -13,7 +14,8 @@ def rng(seed):
     return np.random.default_rng(seed)
 
 
-def test_block_backward_matches_finite_differences():
+@pytest.mark.parametrize("mode", O.SCATTER_MODES)
+def test_block_backward_matches_finite_differences(mode):
     """Every head's selection held fixed: central differences of sum(y * dy)
     with respect to the block input and all four projection weights."""
     r = rng(31)
@@ -22,19 +24,19 @@ def test_block_backward_matches_finite_differences():
     wq, wk, wv = (r.standard_normal((H * d, D)) / np.sqrt(D) for _ in range(3))
     wo = r.standard_normal((D, H * d)) / np.sqrt(H * d)
     dy = r.standard_normal((N, D))
-    y, cache = P.projected_forward(x, wq, wk, wv, wo, H, p, L, S, "f64")
+    y, cache = P.projected_forward(x, wq, wk, wv, wo, H, p, L, S, "f64", mode)
     grads = P.projected_backward(dy, cache, "f64")
     np.testing.assert_allclose(
-        P.projected_forward_fixed(x, wq, wk, wv, wo, cache["fwds"], H, p, L), y, atol=1e-12)
+        P.projected_forward_fixed(x, wq, wk, wv, wo, cache["fwds"], H, p, L, mode), y, atol=1e-12)
     args = [x, wq, wk, wv, wo]
     h = 1e-6
     for which, g in enumerate(grads):
         for idx in np.ndindex(*args[which].shape):
             a = [t.copy() for t in args]
             a[which][idx] += h
-            fp = (P.projected_forward_fixed(*a, cache["fwds"], H, p, L) * dy).sum()
+            fp = (P.projected_forward_fixed(*a, cache["fwds"], H, p, L, mode) * dy).sum()
             a[which][idx] -= 2 * h
-            fm = (P.projected_forward_fixed(*a, cache["fwds"], H, p, L) * dy).sum()
+            fm = (P.projected_forward_fixed(*a, cache["fwds"], H, p, L, mode) * dy).sum()
             assert abs((fp - fm) / (2 * h) - g[idx]) < 1e-6 * (1 + abs(g[idx])), (which, idx)
 
 
