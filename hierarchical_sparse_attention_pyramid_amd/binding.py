@@ -52,7 +52,8 @@ class Buffers(ctypes.Structure):
 
 EXPORTS = ["lh_query_sizes", "lh_last_error", "lh_build_pyramid", "lh_score", "lh_topk",
            "lh_gather", "lh_attention", "lh_scatter", "lh_forward", "lh_scatter_backward",
-           "lh_attention_backward", "lh_gather_backward", "lh_backward", "lh_profile_step"]
+           "lh_attention_backward", "lh_gather_backward", "lh_backward", "lh_profile_step",
+           "lh_topk_noalloc"]
 
 PROFILE_STAGES = ["pyramid_score", "topk", "gather", "attention_fwd", "scatter",
                   "scatter_bwd", "attention_delta", "attention_dkdv", "attention_dq",
@@ -77,6 +78,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "lh_build_pyramid": [sp, P, P, P, P, P, P, P, S, P],
         "lh_score": [sp, P, P, P, P, S, P],
         "lh_topk": [sp, P, P, P, S, P],
+        "lh_topk_noalloc": [sp, P, P, P],
         "lh_gather": [sp, P, P, P, P, P, P, P, P, P, P, P, P, P, S, P],
         "lh_attention": [sp, P, P, P, P, P, P],
         "lh_scatter": [sp, P, P, P, P],
@@ -177,6 +179,11 @@ def lh_score(shape, q, k, score, ws=None, stream=None):
 def lh_topk(shape, score, sel, ws=None, stream=None):
     _check(load_library().lh_topk(ctypes.byref(shape), _ptr(score), _ptr(sel), _ptr(ws),
                                   _nbytes(ws), _stream(stream)))
+
+
+def lh_topk_noalloc(shape, score, sel, stream=None):
+    _check(load_library().lh_topk_noalloc(ctypes.byref(shape), _ptr(score), _ptr(sel),
+                                          _stream(stream)))
 
 
 def lh_gather(shape, sel, q, k, v, pq, pk, pv, sub_idx, pos, qs, ks, vs, ws=None, stream=None):

@@ -4,9 +4,18 @@
 #include "lighthouse.h"
 
 #include <algorithm>
+#include <mutex>
 #include <string>
 
 #include "kernels.h"
+
+// Scratch of lh_topk_noalloc: the top-K workspace in a fixed device array, so
+// that the call allocates nothing.  Each device holds its own copy until the
+// process ends.  Host code never passes the array's name to a kernel (on the
+// host it is a stand-in, not a device address); it uses the address that
+// hipGetSymbolAddress returns for the current device.
+constexpr size_t kNoAllocScratchBytes = size_t(4) << 20;
+static __device__ __align__(256) uint32_t scratch[kNoAllocScratchBytes / sizeof(uint32_t)];
 
 namespace {
 
@@ -332,6 +341,48 @@ lh_status lh_score(const lh_shape* shape, const void* q, const void* k, float* s
   (void)ws_bytes;
   return run_pool(P, q, k, nullptr, nullptr, nullptr, nullptr, score, nullptr, false, true,
                   static_cast<hipStream_t>(stream));
+}
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept for later calls.
+static lh_status noalloc_scratch(void** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(LH_EUNSUPPORTED, "device index above 63");
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return LH_OK;
+}
+
+lh_status lh_topk_noalloc(const lh_shape* shape, const float* score, int32_t* sel,
+                          void* stream) {
+  Plan P;
+  lh_status s = make_plan(shape, P);
+  if (s != LH_OK) return s;
+  if (P.g.K == 0) return LH_OK;
+  LH_NEED(score, "score");
+  LH_NEED(sel, "sel");
+  if (P.sz.ws_topk > kNoAllocScratchBytes)
+    return fail(LH_EWORKSPACE, "lh_topk_noalloc: the top-K needs " + std::to_string(P.sz.ws_topk) +
+                                   " bytes of scratch, above its static " +
+                                   std::to_string(kNoAllocScratchBytes) +
+                                   " bytes; use lh_topk with a workspace");
+  void* ws = nullptr;
+  if ((s = noalloc_scratch(&ws)) != LH_OK) return s;
+  // topk_init clears the histograms and the pick state in a kernel, so what
+  // an earlier call left in the array does not matter
+  LH_HIP(lh::launch_topk(score, sel, ws, P.g, P.BH, static_cast<hipStream_t>(stream)), "topk");
+  return LH_OK;
 }
 
 lh_status lh_topk(const lh_shape* shape, const float* score, int32_t* sel, void* ws,

@@ -176,6 +176,22 @@ lh_status lh_score(const lh_shape *shape, const void *q, const void *k, float *s
 lh_status lh_topk(const lh_shape *shape, const float *score, int32_t *sel, void *ws,
                   size_t ws_bytes, void *stream);
 
+/* lh_topk for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same selection, written to sel exactly as lh_topk writes it, with the
+ * scratch space in a fixed 4 MiB device array of the library instead of a
+ * workspace argument.  The array is per device and lives until the process
+ * ends; the call allocates nothing and frees nothing.  Shapes whose top-K
+ * scratch (lh_sizes.ws_topk) exceeds 4 MiB -- about 160 heads of up to 1M
+ * tokens -- return LH_EWORKSPACE before anything is launched.  Every call on
+ * one device shares that device's array: calls that overlap on one GPU (on
+ * different streams, or from different threads) race and give undefined
+ * results; calls ordered on one stream are safe, and each call clears what
+ * it needs zeroed in a kernel.  The first call on a device looks the array's
+ * address up (hipGetSymbolAddress); a failure there returns LH_EHIP. */
+lh_status lh_topk_noalloc(const lh_shape *shape, const float *score, int32_t *sel,
+                          void *stream);
+
 /* a4. Causal gather (technical summary §2.C; bitsgeniais phase 3): the
  * selected candidates plus every coarsest-level entry, ordered by (end token,
  * level) ascending with end(l,j) = (j+1)*p^l - 1.  Writes sub_idx [B,H,S]
