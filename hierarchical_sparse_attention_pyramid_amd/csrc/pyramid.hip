@@ -219,7 +219,7 @@ __global__ __launch_bounds__(256) void pool_fwd_kernel(PoolFwdArgs a, int do_poo
 // burst, so that no load of a row group waits on a position load.
 constexpr int kBwdPosCache = 4608;  // ints: workgroup rows + their ancestors (p >= 2)
 
-template <typename Tin, typename Tout, bool FIRST>
+template <typename Tin, typename Tout, bool FIRST, int SH>
 __global__ __launch_bounds__(256) void pool_bwd_kernel(PoolBwdArgs a) {
   const Geo& g = a.g;
   const int d = g.d;
@@ -230,11 +230,14 @@ __global__ __launch_bounds__(256) void pool_bwd_kernel(PoolBwdArgs a) {
   const int64_t nchunks = (a.in_rows + a.chunk - 1) / a.chunk;
   const int64_t c = (int64_t)blockIdx.x * rgs + rg;
   const int32_t* pos = a.pos + bh * g.M;
-  const int sh = a.shift;
   // position of virtual entry j of level l (-1: outside the level or not selected)
   auto vpos = [&](int l, int32_t j) {
-    const int32_t jj = j - sh;
-    return jj >= 0 && jj < g.nlev[l] ? pos[g.base[l] + jj] : -1;
+    if constexpr (SH == 0) {
+      return pos[g.base[l] + j];
+    } else {
+      const int32_t jj = j - SH;
+      return jj >= 0 && jj < g.nlev[l] ? pos[g.base[l] + jj] : -1;
+    }
   };
 
   // ---- stage positions: rows [B0, B0 + BT) of level lvl0 (token pass), then
@@ -296,19 +299,19 @@ __global__ __launch_bounds__(256) void pool_bwd_kernel(PoolBwdArgs a) {
 #pragma unroll
     for (int u = 0; u < kRowsInFlight; ++u) {
       const int64_t row = r0 + min(rb + u, nrows - 1);
-      if constexpr (FIRST) {
+      if constexpr (FIRST && SH != 0) {
         // token row of virtual row `row`: zeros before the first token and in the padding
-        const int64_t t = row - sh;
+        const int64_t t = row - SH;
         if (t >= 0 && t < g.N) {
           Row8<Tin>::template load<kStream>(in + t * a.lin.sn, xs[u]);
         } else {
 #pragma unroll
           for (int e = 0; e < 8; ++e) xs[u][e] = 0.f;
         }
-        pt[u] = sp[row - B0];
       } else {
         Row8<Tin>::template load<kStream>(in + row * a.lin.sn, xs[u]);
       }
+      if constexpr (FIRST) pt[u] = sp[row - B0];
     }
 #pragma unroll
     for (int u = 0; u < kRowsInFlight; ++u) {
@@ -325,7 +328,8 @@ __global__ __launch_bounds__(256) void pool_bwd_kernel(PoolBwdArgs a) {
           walk.advance((int32_t)row, posf, nullptr, g, true, lane);
           ct += walk.cnt[1];
         }
-        const float rc = ct > 0 ? 1.0f / static_cast<float>(ct) : 0.0f;
+        // span reading: every token has a contributor; causal: 0 for an unfed token
+        const float rc = SH == 0 || ct > 0 ? 1.0f / static_cast<float>(ct) : 0.0f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) xs[u][e] *= rc;
         if (pt[u] >= 0) Row8<Tout>::store(dos + (int64_t)pt[u] * d, xs[u]);
@@ -379,12 +383,24 @@ hipError_t launch_pool_fwd(const PoolFwdArgs& a, int dtype, int64_t BH, bool fir
 hipError_t launch_pool_bwd(const PoolBwdArgs& a, int dtype, int64_t BH, bool first,
                            hipStream_t st) {
   const dim3 grid = pool_grid(a.in_rows, a.chunk, a.g.d, BH);
+  // the shift is a template parameter: the span reading's kernels carry no
+  // virtual-row bookkeeping at all
   if (dtype == 1) {
-    if (first) pool_bwd_kernel<__bf16, __bf16, true><<<grid, 256, 0, st>>>(a);
-    else pool_bwd_kernel<float, __bf16, false><<<grid, 256, 0, st>>>(a);
+    if (first) {
+      if (a.shift) pool_bwd_kernel<__bf16, __bf16, true, 1><<<grid, 256, 0, st>>>(a);
+      else pool_bwd_kernel<__bf16, __bf16, true, 0><<<grid, 256, 0, st>>>(a);
+    } else {
+      if (a.shift) pool_bwd_kernel<float, __bf16, false, 1><<<grid, 256, 0, st>>>(a);
+      else pool_bwd_kernel<float, __bf16, false, 0><<<grid, 256, 0, st>>>(a);
+    }
   } else {
-    if (first) pool_bwd_kernel<float, float, true><<<grid, 256, 0, st>>>(a);
-    else pool_bwd_kernel<float, float, false><<<grid, 256, 0, st>>>(a);
+    if (first) {
+      if (a.shift) pool_bwd_kernel<float, float, true, 1><<<grid, 256, 0, st>>>(a);
+      else pool_bwd_kernel<float, float, true, 0><<<grid, 256, 0, st>>>(a);
+    } else {
+      if (a.shift) pool_bwd_kernel<float, float, false, 1><<<grid, 256, 0, st>>>(a);
+      else pool_bwd_kernel<float, float, false, 0><<<grid, 256, 0, st>>>(a);
+    }
   }
   return hipGetLastError();
 }

@@ -67,7 +67,7 @@ template <> struct Out4<__bf16> {
   }
 };
 
-template <typename Tout, int NT>
+template <typename Tout, int NT, int SH>
 __global__ __launch_bounds__(256) void bcast_kernel(BcastArgs a) {
   const Geo& g = a.g;
   const int lpr = g.d / kE;
@@ -83,11 +83,14 @@ __global__ __launch_bounds__(256) void bcast_kernel(BcastArgs a) {
     src[i] = a.src[i] + bh * (int64_t)g.S * g.d;
     out[i] = static_cast<Tout*>(a.out[i]) + a.lout.head(bh) + kE * lane;
   }
-  const int sh = a.shift;
-  const int32_t nv = g.N + sh;  // virtual tokens u = t + shift
+  const int32_t nv = g.N + SH;  // virtual tokens u = t + SH
   auto vpos = [&](int l, int32_t j) {
-    const int32_t jj = j - sh;
-    return jj >= 0 && jj < g.nlev[l] ? pos[g.base[l] + jj] : -1;
+    if constexpr (SH == 0) {
+      return pos[g.base[l] + j];
+    } else {
+      const int32_t jj = j - SH;
+      return jj >= 0 && jj < g.nlev[l] ? pos[g.base[l] + jj] : -1;
+    }
   };
   const int32_t t0 = ((int32_t)blockIdx.x * rgs + rg) * kTokPerGroup;
   if (t0 >= nv) return;  // no block-wide barrier in this kernel
@@ -111,15 +114,16 @@ __global__ __launch_bounds__(256) void bcast_kernel(BcastArgs a) {
     for (int u = 0; u < kU; ++u) {
       if (t + u >= t1) break;
       w.advance(t + u, vpos, src, g, mean, lane);
-      if (t + u < sh) continue;  // virtual token 0 of the causal reading: no output row
+      if (SH != 0 && t + u < SH) continue;  // virtual token 0 of the causal reading: no output row
       const int c = w.cnt[1] + (r0[u] >= 0 ? 1 : 0);
-      const float rc = mean ? (c > 0 ? 1.0f / static_cast<float>(c) : 0.0f) : 1.0f;
+      // span reading: every token has a contributor; causal: 0 for an unfed token
+      const float rc = mean ? (SH == 0 || c > 0 ? 1.0f / static_cast<float>(c) : 0.0f) : 1.0f;
 #pragma unroll
       for (int i = 0; i < NT; ++i) {
         float o[kE];
 #pragma unroll
         for (int e = 0; e < kE; ++e) o[e] = (w.A[1][i][e] + v0[u][i][e]) * rc;
-        Out4<Tout>::store(out[i] + (int64_t)(t + u - sh) * a.lout.sn, o);
+        Out4<Tout>::store(out[i] + (int64_t)(t + u - SH) * a.lout.sn, o);
       }
     }
   }
@@ -152,7 +156,7 @@ struct FastBuf {
   int si[kFastInner];
 };
 
-template <typename Tout>
+template <typename Tout, int SH>
 __global__ __launch_bounds__(256) void bcast_fast(BcastArgs a) {
   const Geo& g = a.g;
   const int lpr = g.d / kE;
@@ -164,25 +168,25 @@ __global__ __launch_bounds__(256) void bcast_fast(BcastArgs a) {
   const int32_t B0 = (int32_t)blockIdx.x * BT;
   const int32_t* pos = a.pos + bh * g.M;
   const int lg = g.log2p;
-  const int sh = a.shift;
-  const int32_t nv = g.N + sh;  // virtual tokens u = t + shift
+  const int32_t nv = g.N + SH;  // virtual tokens u = t + SH
   __shared__ int32_t sp[kPosCache];
   __shared__ int32_t soff[kMaxLevels];  // start of level l's run in sp
 
   // ---- stage positions vpos: virtual tokens [B0, B0 + BT), then each
   // level's ancestors of them
   for (int i = threadIdx.x; i < BT; i += 256) {
-    const int32_t t = B0 + i - sh;
-    sp[i] = t >= 0 && t < g.N ? pos[t] : -1;
+    const int32_t t = B0 + i - SH;
+    sp[i] = (SH == 0 || t >= 0) && t < g.N ? pos[t] : -1;
   }
   const int lbt = __builtin_ctz(BT);  // BT is a power of two (64 tokens x 8 or 16 row groups)
   int off = BT;
   for (int l = 1; l < g.L; ++l) {
     const int n = lg * l >= lbt ? 1 : BT >> (lg * l);  // ancestors of the block: max(1, BT / p^l)
-    const int32_t jlo = (B0 >> (lg * l)) - sh;
+    const int32_t jlo = (B0 >> (lg * l)) - SH;
     if (threadIdx.x == 0) soff[l] = off;
     for (int i = threadIdx.x; i < n; i += 256)
-      sp[off + i] = jlo + i >= 0 && jlo + i < g.nlev[l] ? pos[g.base[l] + jlo + i] : -1;
+      sp[off + i] =
+          (SH == 0 || jlo + i >= 0) && jlo + i < g.nlev[l] ? pos[g.base[l] + jlo + i] : -1;
     off += n;
   }
   __syncthreads();
@@ -296,13 +300,15 @@ __global__ __launch_bounds__(256) void bcast_fast(BcastArgs a) {
     for (int u = 0; u < kFastU; ++u) {
       const int32_t t = c + u;
       if (t >= t1) break;
-      if (t < sh) continue;  // virtual token 0 of the causal reading: no output row
+      if (SH != 0 && t < SH) continue;  // virtual token 0 of the causal reading: no output row
       const int cnt = C[0] + b.s0[u];
-      const float rc = mean ? (cnt > 0 ? 1.0f / static_cast<float>(cnt) : 0.0f) : 1.0f;
+      // span reading: every token has a contributor; causal: 0 for an unfed token
+      const float rc =
+          mean ? (SH == 0 || cnt > 0 ? 1.0f / static_cast<float>(cnt) : 0.0f) : 1.0f;
       float o[kE];
 #pragma unroll
       for (int e = 0; e < kE; ++e) o[e] = (A[0][e] + b.r0[u][e]) * rc;
-      Out4<Tout>::store(out + (int64_t)(t - sh) * a.lout.sn, o);
+      Out4<Tout>::store(out + (int64_t)(t - SH) * a.lout.sn, o);
     }
   };
   if (nin == 0) {  // A[0] must be the outer sum
@@ -330,21 +336,31 @@ __global__ __launch_bounds__(256) void bcast_fast(BcastArgs a) {
 hipError_t launch_bcast(const BcastArgs& a, int dtype, int ntensors, int64_t BH, hipStream_t st) {
   const int rgs = 256 / (a.g.d / kE);
   const int64_t nv = (int64_t)a.g.N + a.shift;  // virtual tokens
+  // the shift is a template parameter: the span reading's kernels carry no
+  // virtual-token bookkeeping at all
+  if (a.shift != 0 && (ntensors != 1 || a.mean == 0)) return hipErrorInvalidValue;
   if (LH_BC_FAST && a.g.log2p >= 2) {
     const int64_t bt = (int64_t)rgs * kFastTok;
     const dim3 grid((unsigned)((nv + bt - 1) / bt), (unsigned)BH, (unsigned)ntensors);
-    if (dtype == 1) bcast_fast<__bf16><<<grid, 256, 0, st>>>(a);
-    else bcast_fast<float><<<grid, 256, 0, st>>>(a);
+    if (dtype == 1) {
+      if (a.shift) bcast_fast<__bf16, 1><<<grid, 256, 0, st>>>(a);
+      else bcast_fast<__bf16, 0><<<grid, 256, 0, st>>>(a);
+    } else {
+      if (a.shift) bcast_fast<float, 1><<<grid, 256, 0, st>>>(a);
+      else bcast_fast<float, 0><<<grid, 256, 0, st>>>(a);
+    }
     return hipGetLastError();
   }
   const int64_t per_block = (int64_t)rgs * kTokPerGroup;
   const dim3 grid((unsigned)((nv + per_block - 1) / per_block), (unsigned)BH);
   if (dtype == 1) {
-    if (ntensors == 3) bcast_kernel<__bf16, 3><<<grid, 256, 0, st>>>(a);
-    else bcast_kernel<__bf16, 1><<<grid, 256, 0, st>>>(a);
+    if (ntensors == 3) bcast_kernel<__bf16, 3, 0><<<grid, 256, 0, st>>>(a);
+    else if (a.shift) bcast_kernel<__bf16, 1, 1><<<grid, 256, 0, st>>>(a);
+    else bcast_kernel<__bf16, 1, 0><<<grid, 256, 0, st>>>(a);
   } else {
-    if (ntensors == 3) bcast_kernel<float, 3><<<grid, 256, 0, st>>>(a);
-    else bcast_kernel<float, 1><<<grid, 256, 0, st>>>(a);
+    if (ntensors == 3) bcast_kernel<float, 3, 0><<<grid, 256, 0, st>>>(a);
+    else if (a.shift) bcast_kernel<float, 1, 1><<<grid, 256, 0, st>>>(a);
+    else bcast_kernel<float, 1, 0><<<grid, 256, 0, st>>>(a);
   }
   return hipGetLastError();
 }
