@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "common.h"
 
 namespace lh {
@@ -23,6 +25,11 @@ struct PoolFwdArgs {
   int32_t lvl0;          // level of the input rows
   int32_t lam;           // levels produced: lvl0+1 .. lvl0+lam
   int32_t chunk;         // input rows per row group (a multiple of p^lam)
+  // token pass only: words [zero_off, zero_off + zero_words) of each of
+  // zero_heads heads, zero_stride words apart from `zero`, are cleared (the
+  // top-K histograms of lh_forward); null: nothing
+  uint32_t* zero;
+  int64_t zero_heads, zero_stride, zero_off, zero_words;
   Geo g;
 };
 
@@ -55,10 +62,18 @@ hipError_t launch_pool_bwd(const PoolBwdArgs& a, int dtype, int64_t BH, bool fir
 hipError_t launch_bcast(const BcastArgs& a, int dtype, int ntensors, int64_t BH, hipStream_t st);
 
 // top-K
-int64_t topk_blocks(int64_t C);
+// Heads of at most 16384 candidates are selected in one workgroup's LDS (no
+// workspace); larger ones use a workspace whose words [off, off + words) of
+// each head (stride words apart) must be zero before the selection runs.
+struct TopkZero {
+  int64_t stride, off, words;  // uint32 words; all zero: nothing to clear
+};
+bool topk_small_path(int64_t C);
 size_t topk_ws_bytes(int64_t BH, int64_t C);
+TopkZero topk_zero_region(int64_t C);
+// zeroed: the caller already cleared the region (else a clearing kernel runs first)
 hipError_t launch_topk(const float* score, int32_t* sel, void* ws, const Geo& g, int64_t BH,
-                       hipStream_t st);
+                       bool zeroed, hipStream_t st);
 
 // gather
 // q, k, v: token tensors of layout lq

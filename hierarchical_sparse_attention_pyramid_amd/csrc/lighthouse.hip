@@ -14,7 +14,7 @@
 // process ends.  Host code never passes the array's name to a kernel (on the
 // host it is a stand-in, not a device address); it uses the address that
 // hipGetSymbolAddress returns for the current device.
-constexpr size_t kNoAllocScratchBytes = size_t(4) << 20;
+constexpr size_t kNoAllocScratchBytes = size_t(16) << 20;
 static __device__ __align__(256) uint32_t scratch[kNoAllocScratchBytes / sizeof(uint32_t)];
 
 namespace {
@@ -229,7 +229,9 @@ lh_status make_plan(const lh_shape* s, Plan& P) {
   z.ws_gather = 0;
   z.ws_attention_backward = 2 * align_up(z.bytes_lse);  // rowsum(dO*O), lse*log2(e)
   z.ws_scatter_backward = sums1;
-  z.ws_forward = std::max(z.ws_build_pyramid, z.ws_topk);
+  // the pooling pass clears the top-K histograms while it writes its float32
+  // sums: the two regions must not overlap
+  z.ws_forward = align_up(z.ws_build_pyramid) + z.ws_topk;
   z.ws_backward = align_up(z.bytes_sub) + 3 * align_up(z.bytes_sub_f32) + z.ws_attention_backward +
                   z.ws_scatter_backward;
   return LH_OK;
@@ -269,7 +271,8 @@ lh_status check_ws(void* ws, size_t have, size_t need) {
   } while (0)
 
 lh_status run_pool(const Plan& P, const void* q, const void* k, const void* v, void* pq, void* pk,
-                   void* pv, float* score, void* ws, bool do_pool, bool do_score, hipStream_t st) {
+                   void* pv, float* score, void* ws, bool do_pool, bool do_score, hipStream_t st,
+                   void* topk_ws = nullptr) {
   const void* lvl0[3] = {q, k, v};
   void* pyr[3] = {pq, pk, pv};
   for (int s = 0; s < P.nstages; ++s) {
@@ -289,6 +292,16 @@ lh_status run_pool(const Plan& P, const void* q, const void* k, const void* v, v
     a.lvl0 = t.lvl0;
     a.lam = t.lam;
     a.chunk = t.chunk;
+    if (s == 0 && topk_ws != nullptr) {  // the top-K's histograms start at zero
+      const lh::TopkZero zr = lh::topk_zero_region(P.g.C);
+      if (zr.words > 0) {
+        a.zero = static_cast<uint32_t*>(topk_ws);
+        a.zero_heads = P.BH;
+        a.zero_stride = zr.stride;
+        a.zero_off = zr.off;
+        a.zero_words = zr.words;
+      }
+    }
     a.g = P.g;
     LH_HIP(lh::launch_pool_fwd(a, P.dtype, P.BH, s == 0, do_pool, do_score, st), "pyramid");
   }
@@ -379,9 +392,9 @@ lh_status lh_topk_noalloc(const lh_shape* shape, const float* score, int32_t* se
                                    " bytes; use lh_topk with a workspace");
   void* ws = nullptr;
   if ((s = noalloc_scratch(&ws)) != LH_OK) return s;
-  // topk_init clears the histograms and the pick state in a kernel, so what
-  // an earlier call left in the array does not matter
-  LH_HIP(lh::launch_topk(score, sel, ws, P.g, P.BH, static_cast<hipStream_t>(stream)), "topk");
+  // the top-K clears its histograms in a kernel of its own, so what an
+  // earlier call left in the array does not matter
+  LH_HIP(lh::launch_topk(score, sel, ws, P.g, P.BH, false, static_cast<hipStream_t>(stream)), "topk");
   return LH_OK;
 }
 
@@ -394,7 +407,7 @@ lh_status lh_topk(const lh_shape* shape, const float* score, int32_t* sel, void*
   LH_NEED(score, "score");
   LH_NEED(sel, "sel");
   if ((s = check_ws(ws, ws_bytes, P.sz.ws_topk)) != LH_OK) return s;
-  LH_HIP(lh::launch_topk(score, sel, ws, P.g, P.BH, static_cast<hipStream_t>(stream)), "topk");
+  LH_HIP(lh::launch_topk(score, sel, ws, P.g, P.BH, false, static_cast<hipStream_t>(stream)), "topk");
   return LH_OK;
 }
 
@@ -496,10 +509,13 @@ static lh_status check_forward_args(const Plan& P, const void* q, const void* k,
 static lh_status run_forward(const Plan& P, const void* q, const void* k, const void* v, void* out,
                              const lh_buffers* b, void* ws, hipStream_t st, hipEvent_t* ev) {
   lh_status s;
-  if ((s = run_pool(P, q, k, v, b->pq, b->pk, b->pv, b->score, ws, P.g.L > 1, true, st)) != LH_OK)
+  // the top-K region follows the pooling sums; the pooling pass clears it
+  void* tws = P.g.K > 0 ? static_cast<char*>(ws) + align_up(P.sz.ws_build_pyramid) : nullptr;
+  if ((s = run_pool(P, q, k, v, b->pq, b->pk, b->pv, b->score, ws, P.g.L > 1, true, st, tws)) !=
+      LH_OK)
     return s;
   if (ev) LH_HIP(hipEventRecord(ev[0], st), "event");
-  LH_HIP(lh::launch_topk(b->score, b->sel, ws, P.g, P.BH, st), "topk");
+  LH_HIP(lh::launch_topk(b->score, b->sel, tws, P.g, P.BH, true, st), "topk");
   if (ev) LH_HIP(hipEventRecord(ev[1], st), "event");
   const void* lv0[3] = {q, k, v};
   const void* pyr[3] = {b->pq, b->pk, b->pv};

@@ -182,6 +182,19 @@ __device__ __forceinline__ void pool_pass(const PoolFwdArgs& a, const int (&tid)
 
 template <typename Tin, typename Tout, bool FIRST>
 __global__ __launch_bounds__(256) void pool_fwd_kernel(PoolFwdArgs a, int do_pool, int do_score) {
+  if (FIRST && a.zero != nullptr) {
+    // clear a region for a later kernel of the same call (16-byte stores,
+    // spread over every workgroup of the grid)
+    const int64_t per = a.zero_words / 4;
+    const int64_t total = a.zero_heads * per;
+    const int64_t nthreads = (int64_t)gridDim.x * gridDim.y * blockDim.x;
+    for (int64_t i = ((int64_t)blockIdx.y * gridDim.x + blockIdx.x) * blockDim.x + threadIdx.x;
+         i < total; i += nthreads) {
+      const int64_t h = i / per;
+      reinterpret_cast<uint4*>(a.zero + h * a.zero_stride + a.zero_off)[i - h * per] =
+          make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
   const int lpr = a.g.d / 8;
   const int rgs = 256 / lpr;
   const int rg = threadIdx.x / lpr, lane = threadIdx.x % lpr;

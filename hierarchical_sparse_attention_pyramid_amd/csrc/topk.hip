@@ -6,60 +6,84 @@
 // The gist.science summary (§2.B) and the bitsgeniais post (phase 2) name a
 // fused chunked-bitonic top-K kernel; the operating points they report
 // select k = 1536 candidates.  Here K reaches 32K out of 1.4M candidates per
-// head, so the selection is an exact radix select instead:
-//   1. three histogram passes over the float32 score bits (11 + 11 + 10
-//      bits; scores are non-negative, so their bit patterns order like the
-//      values) find the score T of the K-th candidate and how many
-//      candidates equal to T are still needed;
-//   2. an ordered stream compaction keeps every candidate above T and the
-//      first `need` candidates equal to T in flat order.
-// Both steps are exact integer work and give one deterministic answer.
+// head, so the selection is an exact radix select on the float32 score bits
+// instead (scores are non-negative, so their bit patterns order like the
+// values; other bit patterns rank by their unsigned value).  It finds the
+// score T of the K-th candidate and how many candidates equal to T are
+// still needed (`need`), then keeps every candidate above T and the first
+// `need` equal to T in flat order.  Integer work only: one deterministic
+// answer.
 //
-// Workspace per head (uint32): four (prefix, remaining) pairs, one per pick
-// ([0] from the init, [p + 1] after pass p), three histograms (one per
-// pass), then two arrays of nblk block counters (candidates above and equal
-// to the threshold).  Each pick (the bin holding the K-th candidate) is
-// computed at the start of the launch that needs it, by every block of that
-// launch from the finished histogram, and block 0 records it for the launches
-// after: a "last block finishes the pass" scheme would need a device-scope
-// fence in every block, which on a multi-XCD GPU (one L2 per XCD) costs more
-// than the redundant pick.  Each block of the compaction sums the counters
-// of the blocks before it itself.
+// On this GPU a dependent kernel launch costs about 4-5 us whatever its
+// size, so the design minimises launches rather than bytes:
+//
+//  * C <= 16384 candidates per head: one workgroup per head holds all of
+//    its scores in LDS and runs three histogram passes (11 + 11 + 10 bits)
+//    and the ordered compaction there: one launch, no workspace.
+//  * larger heads: two 16-bit digits, three launches, and no separate
+//    counting pass.
+//      h0: histogram of the top 16 bits (per workgroup a direct-mapped LDS
+//          table of packed 16-bit counters for the few coarse bins -- top 8
+//          bits -- that its slices touch, then integer atomics into the
+//          head's global coarse and fine -- top 16 bits -- histograms);
+//      h1: every workgroup picks the pass-0 bin P0 from those histograms;
+//          then, per 4096-candidate slice, it counts the candidates above
+//          P0 and counting-sorts the ones inside P0 by bits 15..8 into a
+//          per-slice record (offsets E and the low 16 bits of each), adding
+//          the per-bin totals to the head's pass-1 coarse histogram;
+//      w:  each workgroup picks T from the pass-1 coarse histogram and the
+//          records' entries in the chosen coarse bin (usually a handful),
+//          counts the candidates its earlier slices select from the
+//          records alone (the slices' totals above P0, E, and those few
+//          entries), and compacts its own slices in flat order.
+//    The global histograms start each call at zero: in lh_forward the
+//    pooling kernel clears them (it runs first); lh_topk launches a small
+//    clearing kernel of its own.
 #include "kernels.h"
 
 namespace lh {
 
 namespace {
 
-constexpr int kBins = 2048;
-constexpr int kSlice = 4096;  // candidates per block
 constexpr int kThreads = 256;
-constexpr int kHead = 8 + 3 * kBins;  // words before the block counters
-#ifndef LH_TOPK_HIST_BLOCKS
-#define LH_TOPK_HIST_BLOCKS 64
+constexpr int kSlice = 4096;              // candidates per slice
+constexpr int kPer = kSlice / kThreads;   // candidates per thread and slice
+constexpr int kSmallThreads = 1024;
+constexpr int kMaxSub = 15;               // slices per h0 workgroup: its LDS counters are 16-bit
+#ifndef LH_TOPK_WG
+#define LH_TOPK_WG 2048
 #endif
-constexpr int64_t kHistBlocks = LH_TOPK_HIST_BLOCKS;
 
-__device__ __forceinline__ uint32_t* head_ws(void* ws, int64_t bh, int64_t nblk) {
-  return static_cast<uint32_t*>(ws) + bh * (kHead + 2 * nblk);
+// Workspace of the large-head path, per head (uint32 words):
+//   [0, 8)                     header: P0 (pass-0 bin), rem0 (still needed inside it)
+//   [kC0, kC0 + 256)           pass-0 coarse histogram (score bits 31..24)
+//   [kF0, kF0 + 65536)         pass-0 fine histogram (score bits 31..16)
+//   [kC1, kC1 + 256)           pass-1 coarse histogram (bits 15..8 of the candidates in P0)
+//   [kSliceBase + s * kSliceWords, ...) record of slice s:
+//       +0 candidates above P0, +1 candidates inside P0 (n),
+//       +2 E[256] (uint16): entries whose bits 15..8 exceed b start at E[b],
+//       +130 entries[4096] (uint16): low 16 bits, grouped by bits 15..8, descending.
+// Words [kHdr, kZeroEnd) must be zero when h0 starts.
+constexpr int kHdr = 8;
+constexpr int kC0 = kHdr;
+constexpr int kF0 = kC0 + 256;
+constexpr int kC1 = kF0 + 65536;
+constexpr int kZeroEnd = kC1 + 256;
+constexpr int kSliceBase = (kZeroEnd + 63) / 64 * 64;
+constexpr int kRecE = 2;
+constexpr int kRecEnt = 2 + 128;
+constexpr int kSliceWords = kRecEnt + kSlice / 2;
+
+__device__ __forceinline__ uint32_t* head_ws(void* ws, int64_t bh, int64_t stride) {
+  return static_cast<uint32_t*>(ws) + bh * stride;
 }
-__device__ __forceinline__ uint32_t* hist_of(uint32_t* w, int pass) { return w + 8 + pass * kBins; }
-
-__device__ __forceinline__ void pass_bits(int pass, int& shift, int& nbits) {
-  shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
-  nbits = pass == 2 ? 10 : 11;
+__device__ __forceinline__ uint32_t* slice_rec(uint32_t* w, int s) {
+  return w + kSliceBase + (int64_t)s * kSliceWords;
 }
 
-__global__ __launch_bounds__(kThreads) void topk_init(void* ws, int64_t nblk, int32_t K) {
-  uint32_t* w = head_ws(ws, blockIdx.x, nblk);
-  for (int b = threadIdx.x; b < 3 * kBins; b += kThreads) w[8 + b] = 0;
-  if (threadIdx.x == 0) {
-    w[0] = 0;           // threshold prefix
-    w[1] = (uint32_t)K; // candidates still to take at or below the prefix
-  }
-}
-
-// Exclusive prefix sum over the 256 threads of a block (in thread order).
+// Exclusive prefix sum over the NT threads of a block (in thread order);
+// `sh` holds NT / 64 words.  Two barriers.
+template <int NT>
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* sh, uint32_t& total) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   uint32_t x = v;
@@ -73,7 +97,7 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* sh, ui
   uint32_t before = 0;
   total = 0;
 #pragma unroll
-  for (int k = 0; k < kThreads / 64; ++k) {
+  for (int k = 0; k < NT / 64; ++k) {
     if (k < wv) before += sh[k];
     total += sh[k];
   }
@@ -81,219 +105,116 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* sh, ui
   return before + x - v;
 }
 
-// Pick of pass `pass`: the bin of that pass's histogram holding the K-th
-// candidate narrows the prefix.  Every thread of the block returns the new
-// (prefix, remaining); block 0 also records it as pair pass + 1.
-__device__ void pick(uint32_t* w, int pass, uint32_t& prefix_out, uint32_t& rem_out) {
-  __shared__ uint32_t sh[kThreads / 64];
-  __shared__ uint32_t res[2];
-  int shift, nbits;
-  pass_bits(pass, shift, nbits);
-  const int nb = 1 << nbits;
-  const int per = nb / kThreads;
-  const uint32_t* hist = hist_of(w, pass);
-  const uint32_t remaining = w[2 * pass + 1];
-  const uint32_t prefix = w[2 * pass];
-  if (threadIdx.x == 0) {  // overwritten by the thread that finds the bin
-    res[0] = prefix;
-    res[1] = remaining;
-  }
-  // thread t owns bins nb-1-(t*per) down to nb-1-(t*per+per-1): descending;
-  // their counts stay in registers (one round of independent loads)
-  constexpr int kMaxPer = kBins / kThreads;
-  uint32_t cnt[kMaxPer];
-  uint32_t local = 0;
-#pragma unroll
-  for (int j = 0; j < kMaxPer; ++j) {
-    cnt[j] = j < per ? hist[nb - 1 - (threadIdx.x * per + j)] : 0u;
-    local += cnt[j];
+// Descending pick over 256 bins held one per thread (thread t holds bin
+// 255 - t, count c): the bin holding the rem-th largest candidate and how
+// many of that bin are still needed.  Same result in every thread.
+__device__ __forceinline__ void pick256(uint32_t c, uint32_t rem, uint32_t* sh, uint32_t* res,
+                                        uint32_t& bin, uint32_t& rem_out) {
+  if (threadIdx.x == 0) {  // kept if no bin holds it (rem beyond the total: not for valid K)
+    res[0] = 0;
+    res[1] = rem;
   }
   uint32_t total;
-  const uint32_t before = block_excl_scan(local, sh, total);
-  if (before < remaining && remaining <= before + local) {
-    uint32_t cum = before;
-    for (int j = 0; j < per; ++j) {
-      const int b = nb - 1 - (threadIdx.x * per + j);
-      const uint32_t c = cnt[j];
-      if (cum + c >= remaining) {
-        res[0] = prefix | ((uint32_t)b << shift);
-        res[1] = remaining - cum;
-        break;
-      }
-      cum += c;
-    }
+  const uint32_t before = block_excl_scan<kThreads>(c, sh, total);  // its barriers order res
+  if (before < rem && rem <= before + c) {
+    res[0] = 255 - threadIdx.x;
+    res[1] = rem - before;
   }
   __syncthreads();
-  prefix_out = res[0];
+  bin = res[0];
   rem_out = res[1];
-  if (blockIdx.x == 0 && threadIdx.x == 0) {
-    w[2 * pass + 2] = prefix_out;
-    w[2 * pass + 3] = rem_out;
-  }
+  __syncthreads();  // res may be reused
 }
 
-// This thread's candidates of the block's slice (i0 + tid + 256 r), loaded
-// at once; positions past C read as 0 and are excluded by the callers' bounds
-// tests.
-__device__ __forceinline__ void load_slice(const float* s, int i0, int C, uint32_t (&u)[kSlice / kThreads]) {
+// Candidates i0 + r * 256 + t of a slice (lane-consecutive loads); past C: 0.
+__device__ __forceinline__ void load_slice(const float* s, int i0, int C, uint32_t (&u)[kPer]) {
 #pragma unroll
-  for (int r = 0; r < kSlice / kThreads; ++r) {
+  for (int r = 0; r < kPer; ++r) {
     const int i = i0 + r * kThreads + (int)threadIdx.x;
     u[r] = i < C ? __float_as_uint(s[i]) : 0u;
   }
 }
 
-// Histogram pass `pass` over `nsub` consecutive slices (LDS bins, then
-// integer atomics into the head's histogram of that pass), after the pick of
-// the pass before.  The first slice's scores are loaded before the pick, so
-// the two latencies overlap, and each next slice is loaded while the current
-// one is binned.  Several slices per block keep the number of blocks (each
-// clears, flushes and picks over the whole bin range) low on long inputs.
-__global__ __launch_bounds__(kThreads) void topk_hist(const float* score, void* ws, int64_t nblk,
-                                                      int32_t M, int32_t C, int pass, int nsub) {
-  constexpr int kPer = kSlice / kThreads;
-  __shared__ uint32_t h[kBins];
-  const int64_t bh = blockIdx.y;
-  uint32_t* w = head_ws(ws, bh, nblk);
-  int shift, nbits;
-  pass_bits(pass, shift, nbits);
-  const uint32_t mask = (1u << nbits) - 1u;
-  const int hi = shift + nbits;
+// ---------------------------------------------------------------------------
+// Small heads: everything in one workgroup's LDS.
+constexpr int kSmallC = 16384;
+
+__global__ __launch_bounds__(kSmallThreads) void topk_small(const float* score, int32_t* sel,
+                                                            int32_t M, int32_t C, int32_t K) {
+  constexpr int NT = kSmallThreads;
+  __shared__ uint32_t keys[kSmallC];
+  __shared__ uint32_t hist[2048];
+  __shared__ uint32_t sh[NT / 64];
+  __shared__ uint32_t res[2];
+  const int64_t bh = blockIdx.x;
   const float* s = score + bh * M;
-  const int b0 = blockIdx.x * nsub;  // first slice
-  uint32_t u[kPer];
-  load_slice(s, b0 * kSlice, C, u);
-  for (int b = threadIdx.x; b < kBins; b += kThreads) h[b] = 0;
-  uint32_t prefix = 0, rem;
-  if (pass > 0) pick(w, pass - 1, prefix, rem);  // its barriers also order the zeroing
-  else __syncthreads();
-  auto bin = [&](int i0) {
-#pragma unroll
-    for (int r = 0; r < kPer; ++r) {
-      const bool valid = i0 + r * kThreads + (int)threadIdx.x < C;
-      if (valid && (hi >= 32 || ((u[r] ^ prefix) >> hi) == 0u)) atomicAdd(&h[(u[r] >> shift) & mask], 1u);
+  for (int i = threadIdx.x; i < C; i += NT) keys[i] = __float_as_uint(s[i]);
+  uint32_t prefix = 0, rem = (uint32_t)K;
+  for (int pass = 0; pass < 3; ++pass) {
+    const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+    const int nbits = pass == 2 ? 10 : 11;
+    const int nb = 1 << nbits;
+    const int hi = shift + nbits;
+    for (int b = threadIdx.x; b < 2048; b += NT) hist[b] = 0;
+    __syncthreads();  // also publishes keys (first pass)
+    for (int i = threadIdx.x; i < C; i += NT) {
+      const uint32_t u = keys[i];
+      if (hi >= 32 || ((u ^ prefix) >> hi) == 0u) atomicAdd(&hist[(u >> shift) & (nb - 1)], 1u);
     }
-  };
-  if (nsub == 1) {
-    bin(b0 * kSlice);
-  } else {
-    for (int j = 0; j < nsub; ++j) {
-      const int i0 = (b0 + j) * kSlice;
-      if (i0 >= C) break;
-      uint32_t nx[kPer];
-      const bool more = j + 1 < nsub && i0 + kSlice < C;
-      if (more) load_slice(s, i0 + kSlice, C, nx);
-      bin(i0);
-      if (more) {
+    if (threadIdx.x == 0) {
+      res[0] = prefix;
+      res[1] = rem;
+    }
+    __syncthreads();
+    // thread t owns bins nb-1-t*per .. nb-per-t*per (descending)
+    const int per = nb / NT;
+    uint32_t cnt[2] = {0u, 0u};
+    uint32_t local = 0;
 #pragma unroll
-        for (int r = 0; r < kPer; ++r) u[r] = nx[r];
+    for (int j = 0; j < 2; ++j) {
+      if (j < per) cnt[j] = hist[nb - 1 - ((int)threadIdx.x * per + j)];
+      local += cnt[j];
+    }
+    uint32_t total;
+    const uint32_t before = block_excl_scan<NT>(local, sh, total);
+    if (before < rem && rem <= before + local) {
+      uint32_t cum = before;
+      for (int j = 0; j < per; ++j) {
+        const uint32_t c = cnt[j];
+        if (cum + c >= rem) {
+          res[0] = prefix | ((uint32_t)(nb - 1 - ((int)threadIdx.x * per + j)) << shift);
+          res[1] = rem - cum;
+          break;
+        }
+        cum += c;
       }
     }
+    __syncthreads();
+    prefix = res[0];
+    rem = res[1];
+    __syncthreads();
   }
-  __syncthreads();
-  uint32_t* g = hist_of(w, pass);
-  for (int b = threadIdx.x; b < kBins; b += kThreads)
-    if (h[b]) atomicAdd(&g[b], h[b]);
-}
-
-// Last pick, then per-block counts of candidates above and equal to the
-// threshold (scores loaded before the pick, as in the histogram passes).
-__global__ __launch_bounds__(kThreads) void topk_count(const float* score, void* ws, int64_t nblk,
-                                                       int32_t M, int32_t C) {
-  constexpr int kPer = kSlice / kThreads;
-  __shared__ uint32_t sh[kThreads / 64];
-  const int64_t bh = blockIdx.y;
-  uint32_t* w = head_ws(ws, bh, nblk);
-  const int i0 = blockIdx.x * kSlice;
-  uint32_t u[kPer];
-  load_slice(score + bh * M, i0, C, u);
-  uint32_t T, need;
-  pick(w, 2, T, need);
-  uint32_t gt = 0, eq = 0;
-#pragma unroll
-  for (int r = 0; r < kPer; ++r) {
-    const bool valid = i0 + r * kThreads + (int)threadIdx.x < C;
-    gt += (valid && u[r] > T) ? 1u : 0u;
-    eq += (valid && u[r] == T) ? 1u : 0u;
-  }
-  uint32_t tg, te;
-  block_excl_scan(gt, sh, tg);
-  block_excl_scan(eq, sh, te);
-  if (threadIdx.x == 0) {
-    uint32_t* blk = w + kHead;
-    blk[blockIdx.x] = tg;
-    blk[nblk + blockIdx.x] = te;
-  }
-}
-
-// Ordered compaction of one block's slice: thread t owns the contiguous
-// candidates i0 + 16t .. i0 + 16t + 15, so two block scans (equal-to-T ranks,
-// then output offsets) order the whole slice.  The slice's first output
-// position follows from the earlier slices' counts alone: every candidate
-// above T is taken, and candidates equal to T are taken in flat order until
-// `need` of them are in, so the earlier slices took GT + min(EQ, need) of
-// them (GT, EQ: their counts above and equal to T).
-__global__ __launch_bounds__(kThreads) void topk_write(const float* score, int32_t* sel, void* ws,
-                                                       int64_t nblk, int32_t M, int32_t C,
-                                                       int32_t K) {
-  constexpr int kPer = kSlice / kThreads;
-  __shared__ uint32_t sh[kThreads / 64];
-  __shared__ uint4 tile[kSlice / 4];  // the slice's score bits, in flat order
-  const int64_t bh = blockIdx.y;
-  const uint32_t* w = head_ws(ws, bh, nblk);
-  int32_t* out = sel + bh * K;
-  const int i0 = blockIdx.x * kSlice;
-  const int i1 = min(i0 + kSlice, C);
-  const int first = i0 + threadIdx.x * kPer;
-  const int cnt = max(0, min(kPer, i1 - first));  // valid candidates of this thread
-  {
-    // coalesced loads (lane-consecutive), then through LDS to the thread
-    // that owns them; loaded first: independent of the counters below
-    uint32_t v[kPer];
-    load_slice(score + bh * M, i0, C, v);
-    uint32_t* t32 = reinterpret_cast<uint32_t*>(tile);
-#pragma unroll
-    for (int r = 0; r < kPer; ++r) t32[r * kThreads + threadIdx.x] = v[r];
-  }
-  const uint32_t T = w[6], need = w[7];  // the last pick's pair
-  const uint32_t* blk = w + kHead;
-  uint32_t gt_part = 0, eq_part = 0;  // this thread's share of the earlier slices' counts
-  for (int64_t b = threadIdx.x; b < blockIdx.x; b += kThreads) {
-    gt_part += blk[b];
-    eq_part += blk[nblk + b];
-  }
-  uint32_t total;
-  block_excl_scan(gt_part, sh, total);  // its barriers also publish the tile
-  const uint32_t gt_before = total;
-  block_excl_scan(eq_part, sh, total);
-  const uint32_t eqb = total;  // candidates equal to T in the earlier slices
-  const uint32_t off = gt_before + (eqb < need ? eqb : need);
-  uint32_t u[kPer];
-#pragma unroll
-  for (int q = 0; q < kPer / 4; ++q) {
-    const uint4 x = tile[threadIdx.x * (kPer / 4) + q];
-    u[4 * q] = x.x;
-    u[4 * q + 1] = x.y;
-    u[4 * q + 2] = x.z;
-    u[4 * q + 3] = x.w;
-  }
+  const uint32_t T = prefix, need = rem;
+  // ordered compaction: thread t owns the candidates t*E .. t*E + E - 1
+  const int E = (C + NT - 1) / NT;  // <= 16
+  const int first = (int)threadIdx.x * E;
+  const int cnt = max(0, min(E, C - first));
   uint32_t neq = 0;
-#pragma unroll
-  for (int r = 0; r < kPer; ++r) neq += (r < cnt && u[r] == T) ? 1u : 0u;
-  uint32_t eqr = eqb + block_excl_scan(neq, sh, total);  // equal candidates before this thread
+  for (int r = 0; r < cnt; ++r) neq += keys[first + r] == T ? 1u : 0u;
+  uint32_t total;
+  uint32_t eqr = block_excl_scan<NT>(neq, sh, total);
   uint32_t take = 0, ntake = 0;
-#pragma unroll
-  for (int r = 0; r < kPer; ++r) {
-    const bool valid = r < cnt;
-    const bool is_eq = valid && u[r] == T;
-    const bool t = (valid && u[r] > T) || (is_eq && eqr < need);
+  for (int r = 0; r < cnt; ++r) {
+    const uint32_t u = keys[first + r];
+    const bool is_eq = u == T;
+    const bool t = u > T || (is_eq && eqr < need);
     eqr += is_eq ? 1u : 0u;
     take |= (t ? 1u : 0u) << r;
     ntake += t ? 1u : 0u;
   }
-  uint32_t o = off + block_excl_scan(ntake, sh, total);
-#pragma unroll
-  for (int r = 0; r < kPer; ++r) {
+  uint32_t o = block_excl_scan<NT>(ntake, sh, total);
+  int32_t* out = sel + bh * K;
+  for (int r = 0; r < cnt; ++r) {
     if ((take >> r) & 1u) {
       if (o < (uint32_t)K) out[o] = first + r;  // bound: never past K
       ++o;
@@ -301,27 +222,329 @@ __global__ __launch_bounds__(kThreads) void topk_write(const float* score, int32
   }
 }
 
+// ---------------------------------------------------------------------------
+// Large heads.
+
+// Clears words [kHdr, kZeroEnd) of every head (lh_topk only; in lh_forward
+// the pooling kernel does it).
+__global__ __launch_bounds__(kThreads) void topk_zero(void* ws, int64_t stride) {
+  constexpr int kVec = (kZeroEnd - kHdr) / 4;
+  uint4* z = reinterpret_cast<uint4*>(head_ws(ws, blockIdx.y, stride) + kHdr);
+  for (int i = blockIdx.x * kThreads + threadIdx.x; i < kVec; i += gridDim.x * kThreads)
+    z[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+// Pass 0: histogram of bits 31..16 over slices [s0, s1) of one head.  The
+// LDS table is direct-mapped: coarse bin c (score bits 31..24) counts in slot
+// c % kSlots, which the first candidate of that bin claims with a
+// compare-and-swap of the slot's tag; a candidate whose slot another coarse
+// bin holds goes straight to the global histograms.  Scores of one layer span
+// a few adjacent coarse bins, so collisions do not occur in practice, and the
+// slice loop needs no barrier.  The flush adds each pair of adjacent fine
+// bins with one 64-bit atomic (the global fine histogram is read as 32-bit
+// counts; a pair's low count never carries into the high one).
+constexpr int kSlots = 16;
+constexpr uint32_t kFree = 0xFFFFFFFFu;
+
+__global__ __launch_bounds__(kThreads) void topk_h0(const float* score, void* ws, int64_t stride,
+                                                    int32_t M, int32_t C, int32_t nsl, int32_t nsub) {
+  __shared__ uint32_t lf[kSlots * 128];  // bin f of slot k: half f & 1 of word k*128 + (f & 255) / 2
+  __shared__ uint32_t tag[kSlots];       // coarse bin counted in each slot, or kFree
+  __shared__ uint32_t lc[kSlots];        // per slot totals
+  const int64_t bh = blockIdx.y;
+  uint32_t* w = head_ws(ws, bh, stride);
+  const float* s = score + bh * M;
+  const int t = threadIdx.x;
+  const int s0 = blockIdx.x * nsub, s1 = min(s0 + nsub, nsl);
+  uint32_t u[kPer];
+  if (s0 < s1) load_slice(s, s0 * kSlice, C, u);
+  for (int i = t; i < kSlots * 32; i += kThreads)
+    reinterpret_cast<uint4*>(lf)[i] = make_uint4(0u, 0u, 0u, 0u);
+  if (t < kSlots) {
+    tag[t] = kFree;
+    lc[t] = 0u;
+  }
+  __syncthreads();
+  for (int sl = s0; sl < s1; ++sl) {
+    const int i0 = sl * kSlice;
+    uint32_t nx[kPer];
+    const bool more = sl + 1 < s1;
+    if (more) load_slice(s, (sl + 1) * kSlice, C, nx);
+#pragma unroll
+    for (int r = 0; r < kPer; ++r) {
+      if (i0 + r * kThreads + t < C) {
+        const uint32_t f = u[r] >> 16, c = f >> 8, k = c % kSlots;
+        uint32_t tg = tag[k];
+        if (tg == kFree) {
+          const uint32_t old = atomicCAS(&tag[k], kFree, c);
+          tg = old == kFree ? c : old;
+        }
+        if (tg == c) {
+          atomicAdd(&lf[k * 128 + ((f & 255u) >> 1)], (f & 1u) ? 0x10000u : 1u);
+        } else {  // the slot holds another coarse bin: straight to the global histograms
+          atomicAdd(&w[kF0 + f], 1u);
+          atomicAdd(&w[kC0 + c], 1u);
+        }
+      }
+    }
+    if (more) {
+#pragma unroll
+      for (int r = 0; r < kPer; ++r) u[r] = nx[r];
+    }
+  }
+  __syncthreads();
+  // flush the claimed slots
+  for (int i = t; i < kSlots * 128; i += kThreads) {
+    const int k = i >> 7;
+    const uint32_t v = lf[i];
+    if (v) {
+      const uint32_t lo = v & 0xFFFFu, hi = v >> 16;
+      const uint32_t f = (tag[k] << 8) | ((uint32_t)(i & 127) << 1);
+      atomicAdd(reinterpret_cast<unsigned long long*>(w + kF0 + f),
+                ((unsigned long long)hi << 32) | lo);
+      atomicAdd(&lc[k], lo + hi);
+    }
+  }
+  __syncthreads();
+  if (t < kSlots && lc[t]) atomicAdd(&w[kC0 + tag[t]], lc[t]);
+}
+
+// Pick of pass 0, then the per-slice records and the pass-1 coarse histogram.
+__global__ __launch_bounds__(kThreads) void topk_h1(const float* score, void* ws, int64_t stride,
+                                                    int32_t M, int32_t C, int32_t K, int32_t nsl,
+                                                    int32_t nsub) {
+  __shared__ uint32_t sh[kThreads / 64];
+  __shared__ uint32_t res[2];
+  __shared__ uint32_t cnt[256], cur[256];
+  const int64_t bh = blockIdx.y;
+  uint32_t* w = head_ws(ws, bh, stride);
+  const float* s = score + bh * M;
+  const int s0 = blockIdx.x * nsub, s1 = min(s0 + nsub, nsl);
+  uint32_t u[kPer];
+  if (s0 < s1) load_slice(s, s0 * kSlice, C, u);  // overlaps the pick's loads
+  const int t = threadIdx.x;
+  uint32_t cb, r1, fb, rem0;
+  pick256(w[kC0 + 255 - t], (uint32_t)K, sh, res, cb, r1);
+  pick256(w[kF0 + (cb << 8) + 255 - t], r1, sh, res, fb, rem0);
+  const uint32_t P0 = (cb << 8) | fb;
+  if (blockIdx.x == 0 && t == 0) {
+    w[0] = P0;
+    w[1] = rem0;
+  }
+  for (int sl = s0; sl < s1; ++sl) {
+    const int i0 = sl * kSlice;
+    cnt[t] = 0u;
+    __syncthreads();
+    uint32_t gt = 0;
+#pragma unroll
+    for (int r = 0; r < kPer; ++r) {
+      if (i0 + r * kThreads + t < C) {
+        const uint32_t k16 = u[r] >> 16;
+        gt += k16 > P0 ? 1u : 0u;
+        if (k16 == P0) atomicAdd(&cnt[(u[r] >> 8) & 255u], 1u);
+      }
+    }
+    __syncthreads();
+    uint32_t* rec = slice_rec(w, sl);
+    const uint32_t c = cnt[255 - t];
+    uint32_t n;
+    const uint32_t before = block_excl_scan<kThreads>(c, sh, n);  // entries above bin 255 - t
+    reinterpret_cast<uint16_t*>(rec + kRecE)[255 - t] = (uint16_t)before;
+    cur[255 - t] = before;
+    if (c) atomicAdd(&w[kC1 + 255 - t], c);
+    uint32_t gtot;
+    block_excl_scan<kThreads>(gt, sh, gtot);  // its barriers also publish cur
+    if (t == 0) {
+      rec[0] = gtot;
+      rec[1] = n;
+    }
+    uint16_t* ent = reinterpret_cast<uint16_t*>(rec + kRecEnt);
+    uint32_t nx[kPer];
+    const bool more = sl + 1 < s1;
+    if (more) load_slice(s, (sl + 1) * kSlice, C, nx);
+#pragma unroll
+    for (int r = 0; r < kPer; ++r) {
+      if (i0 + r * kThreads + t < C && (u[r] >> 16) == P0) {
+        const uint32_t slot = atomicAdd(&cur[(u[r] >> 8) & 255u], 1u);
+        ent[slot] = (uint16_t)(u[r] & 0xFFFFu);
+      }
+    }
+    if (more) {
+#pragma unroll
+      for (int r = 0; r < kPer; ++r) u[r] = nx[r];
+    }
+    __syncthreads();  // cnt and cur are rewritten by the next slice
+  }
+}
+
+// Pick of T, offsets from the earlier slices' records, ordered compaction of
+// this workgroup's slices [s0, s1).
+__global__ __launch_bounds__(kThreads) void topk_w(const float* score, int32_t* sel, void* ws,
+                                                   int64_t stride, int32_t M, int32_t C, int32_t K,
+                                                   int32_t nsl, int32_t spw) {
+  constexpr int kList = 2048;  // earlier slices' entries of the chosen coarse bin kept in LDS
+  __shared__ uint32_t sh[kThreads / 64];
+  __shared__ uint32_t res[2];
+  __shared__ uint32_t fh[256];
+  __shared__ uint8_t early[kList];
+  __shared__ uint32_t nearly;
+  __shared__ uint4 tile[kSlice / 4];  // a slice's score bits in flat order
+  const int64_t bh = blockIdx.y;
+  const int s0 = blockIdx.x * spw, s1 = min(s0 + spw, nsl);
+  if (s0 >= s1) return;  // uniform per workgroup
+  uint32_t* w = head_ws(ws, bh, stride);
+  const float* s = score + bh * M;
+  int32_t* out = sel + bh * K;
+  const int t = threadIdx.x;
+  uint32_t v[kPer];
+  load_slice(s, s0 * kSlice, C, v);  // the first own slice, ahead of the picks
+  const uint32_t P0 = w[0], rem0 = w[1];
+  fh[t] = 0u;
+  if (t == 0) nearly = 0u;
+  uint32_t thi, r1, tlo, need;
+  pick256(w[kC1 + 255 - t], rem0, sh, res, thi, r1);  // its barriers publish fh, nearly
+  // one pass over every slice's record: fine counts of the entries in coarse
+  // bin thi; for the slices before s0 also the candidates above that bin and
+  // (in LDS) those entries' low bytes
+  uint32_t gt_part = 0;
+  for (int q = t; q < nsl; q += kThreads) {
+    const uint32_t* rec = slice_rec(w, q);
+    const uint16_t* E = reinterpret_cast<const uint16_t*>(rec + kRecE);
+    const uint16_t* ent = reinterpret_cast<const uint16_t*>(rec + kRecEnt);
+    const uint32_t lo = E[thi], hi = thi > 0 ? E[thi - 1] : rec[1];
+    if (q < s0) gt_part += rec[0] + lo;
+    for (uint32_t i = lo; i < hi; ++i) {
+      const uint32_t x = ent[i] & 255u;
+      atomicAdd(&fh[x], 1u);
+      if (q < s0) {
+        const uint32_t j = atomicAdd(&nearly, 1u);
+        if (j < kList) early[j] = (uint8_t)x;
+      }
+    }
+  }
+  __syncthreads();
+  pick256(fh[255 - t], r1, sh, res, tlo, need);
+  const uint32_t T = (P0 << 16) | (thi << 8) | tlo;
+  uint32_t eq_part = 0;
+  if (nearly <= kList) {
+    for (uint32_t i = t; i < nearly; i += kThreads) {
+      const uint32_t x = early[i];
+      gt_part += x > tlo ? 1u : 0u;
+      eq_part += x == tlo ? 1u : 0u;
+    }
+  } else {  // more than the LDS list holds (many equal scores): read them again
+    for (int q = t; q < s0; q += kThreads) {
+      const uint32_t* rec = slice_rec(w, q);
+      const uint16_t* E = reinterpret_cast<const uint16_t*>(rec + kRecE);
+      const uint16_t* ent = reinterpret_cast<const uint16_t*>(rec + kRecEnt);
+      const uint32_t lo = E[thi], hi = thi > 0 ? E[thi - 1] : rec[1];
+      for (uint32_t i = lo; i < hi; ++i) {
+        const uint32_t x = ent[i] & 255u;
+        gt_part += x > tlo ? 1u : 0u;
+        eq_part += x == tlo ? 1u : 0u;
+      }
+    }
+  }
+  uint32_t gtb, eqb;
+  block_excl_scan<kThreads>(gt_part, sh, gtb);
+  block_excl_scan<kThreads>(eq_part, sh, eqb);
+  uint32_t off = gtb + (eqb < need ? eqb : need);
+  for (int sl = s0; sl < s1; ++sl) {
+    const int i0 = sl * kSlice;
+    const int first = i0 + t * kPer;
+    const int cnt = max(0, min(kPer, C - first));
+    if (sl > s0) load_slice(s, i0, C, v);
+    {
+      uint32_t* t32 = reinterpret_cast<uint32_t*>(tile);
+#pragma unroll
+      for (int r = 0; r < kPer; ++r) t32[r * kThreads + t] = v[r];
+    }
+    __syncthreads();
+    uint32_t u[kPer];
+#pragma unroll
+    for (int q = 0; q < kPer / 4; ++q) {
+      const uint4 x = tile[t * (kPer / 4) + q];
+      u[4 * q] = x.x;
+      u[4 * q + 1] = x.y;
+      u[4 * q + 2] = x.z;
+      u[4 * q + 3] = x.w;
+    }
+    uint32_t neq = 0;
+#pragma unroll
+    for (int r = 0; r < kPer; ++r) neq += (r < cnt && u[r] == T) ? 1u : 0u;
+    uint32_t eq_slice;
+    uint32_t eqr = eqb + block_excl_scan<kThreads>(neq, sh, eq_slice);
+    uint32_t take = 0, ntake = 0;
+#pragma unroll
+    for (int r = 0; r < kPer; ++r) {
+      const bool valid = r < cnt;
+      const bool is_eq = valid && u[r] == T;
+      const bool tk = (valid && u[r] > T) || (is_eq && eqr < need);
+      eqr += is_eq ? 1u : 0u;
+      take |= (tk ? 1u : 0u) << r;
+      ntake += tk ? 1u : 0u;
+    }
+    uint32_t take_slice;
+    uint32_t o = off + block_excl_scan<kThreads>(ntake, sh, take_slice);
+#pragma unroll
+    for (int r = 0; r < kPer; ++r) {
+      if ((take >> r) & 1u) {
+        if (o < (uint32_t)K) out[o] = first + r;  // bound: never past K
+        ++o;
+      }
+    }
+    eqb += eq_slice;
+    off += take_slice;
+    // the scans' barriers keep the tile alive until every thread has read it
+  }
+}
+
+int64_t nslices(int64_t C) { return (C + kSlice - 1) / kSlice; }
+
+int64_t head_stride(int64_t C) {
+  return (kSliceBase + nslices(C) * kSliceWords + 63) / 64 * 64;
+}
+
 }  // namespace
 
-int64_t topk_blocks(int64_t C) { return (C + kSlice - 1) / kSlice; }
+bool topk_small_path(int64_t C) { return C <= kSmallC; }
 
 size_t topk_ws_bytes(int64_t BH, int64_t C) {
-  return (size_t)BH * (size_t)(kHead + 2 * topk_blocks(C)) * sizeof(uint32_t);
+  return topk_small_path(C) ? 0 : (size_t)BH * (size_t)head_stride(C) * sizeof(uint32_t);
+}
+
+TopkZero topk_zero_region(int64_t C) {
+  if (topk_small_path(C)) return TopkZero{0, 0, 0};
+  return TopkZero{head_stride(C), kHdr, kZeroEnd - kHdr};
 }
 
 hipError_t launch_topk(const float* score, int32_t* sel, void* ws, const Geo& g, int64_t BH,
-                       hipStream_t st) {
+                       bool zeroed, hipStream_t st) {
   if (g.K == 0) return hipSuccess;
-  const int64_t nblk = topk_blocks(g.C);
-  const dim3 grid((unsigned)nblk, (unsigned)BH);
-  topk_init<<<(unsigned)BH, kThreads, 0, st>>>(ws, nblk, g.K);
-  // at most kHistBlocks histogram blocks per head
-  const int nsub = (int)((nblk + kHistBlocks - 1) / kHistBlocks);
-  const dim3 hgrid((unsigned)((nblk + nsub - 1) / nsub), (unsigned)BH);
-  for (int pass = 0; pass < 3; ++pass)
-    topk_hist<<<hgrid, kThreads, 0, st>>>(score, ws, nblk, g.M, g.C, pass, nsub);
-  topk_count<<<grid, kThreads, 0, st>>>(score, ws, nblk, g.M, g.C);
-  topk_write<<<grid, kThreads, 0, st>>>(score, sel, ws, nblk, g.M, g.C, g.K);
+  if (topk_small_path(g.C)) {
+    topk_small<<<(unsigned)BH, kSmallThreads, 0, st>>>(score, sel, g.M, g.C, g.K);
+    return hipGetLastError();
+  }
+  const int64_t stride = head_stride(g.C);
+  const int64_t nsl = nslices(g.C);
+  if (!zeroed) topk_zero<<<dim3(16, (unsigned)BH), kThreads, 0, st>>>(ws, stride);
+  // workgroups of one slice each, up to about LH_TOPK_WG in all (the
+  // kernels are bound by per-slice latency, not bandwidth); h0 takes at most
+  // kMaxSub slices per workgroup (16-bit LDS counters)
+  const int64_t want = std::max<int64_t>(1, (LH_TOPK_WG + BH - 1) / BH);
+  const int64_t hb0 = std::min<int64_t>(nsl, std::max<int64_t>(want, (nsl + kMaxSub - 1) / kMaxSub));
+  const int64_t nsub0 = (nsl + hb0 - 1) / hb0;
+  topk_h0<<<dim3((unsigned)((nsl + nsub0 - 1) / nsub0), (unsigned)BH), kThreads, 0, st>>>(
+      score, ws, stride, g.M, g.C, (int32_t)nsl, (int32_t)nsub0);
+  const int64_t hb1 = std::min<int64_t>(nsl, want);
+  const int64_t nsub1 = (nsl + hb1 - 1) / hb1;
+  topk_h1<<<dim3((unsigned)((nsl + nsub1 - 1) / nsub1), (unsigned)BH), kThreads, 0, st>>>(
+      score, ws, stride, g.M, g.C, g.K, (int32_t)nsl, (int32_t)nsub1);
+  const int64_t wb = std::min<int64_t>(nsl, want);
+  const int64_t spw = (nsl + wb - 1) / wb;
+  const dim3 wgrid((unsigned)((nsl + spw - 1) / spw), (unsigned)BH);
+  topk_w<<<wgrid, kThreads, 0, st>>>(score, sel, ws, stride, g.M, g.C, g.K, (int32_t)nsl,
+                                     (int32_t)spw);
   return hipGetLastError();
 }
 

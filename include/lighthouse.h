@@ -179,11 +179,12 @@ lh_status lh_topk(const lh_shape *shape, const float *score, int32_t *sel, void 
 /* lh_topk for callers that cannot allocate device memory (code under HIP
  * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
  * same selection, written to sel exactly as lh_topk writes it, with the
- * scratch space in a fixed 4 MiB device array of the library instead of a
+ * scratch space in a fixed 16 MiB device array of the library instead of a
  * workspace argument.  The array is per device and lives until the process
  * ends; the call allocates nothing and frees nothing.  Shapes whose top-K
- * scratch (lh_sizes.ws_topk) exceeds 4 MiB -- about 160 heads of up to 1M
- * tokens -- return LH_EWORKSPACE before anything is launched.  Every call on
+ * scratch (lh_sizes.ws_topk) exceeds 16 MiB -- above about 30 heads of 98K
+ * tokens or 5 heads of 1M tokens; heads of at most 16384 candidates need none
+ * -- return LH_EWORKSPACE before anything is launched.  Every call on
  * one device shares that device's array: calls that overlap on one GPU (on
  * different streams, or from different threads) race and give undefined
  * results; calls ordered on one stream are safe, and each call clears what

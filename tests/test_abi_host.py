@@ -77,10 +77,14 @@ def test_null_pointers_and_small_workspace_are_rejected_without_a_gpu(lb):
     # null q: rejected on the host, nothing launched
     st = lib.lh_build_pyramid(ctypes.byref(shape), None, 1, 1, 1, 1, 1, 1, 1 << 20, None)
     assert st == 1 and b"q is null" in lib.lh_last_error()
-    # workspace too small for the top-K
-    z = lb.lh_query_sizes(shape)
-    st = lib.lh_topk(ctypes.byref(shape), 1, 1, 1, z.ws_topk - 1, None)
+    # workspace too small for the top-K (heads above 16384 candidates need one)
+    big = lb.make_shape(1, 2, 98304, 64, 4, 5, 8192, 1)
+    zb = lb.lh_query_sizes(big)
+    assert zb.ws_topk > 0
+    st = lib.lh_topk(ctypes.byref(big), 1, 1, 1, zb.ws_topk - 1, None)
     assert st == 3
+    z = lb.lh_query_sizes(shape)
+    assert z.ws_topk == 0  # small heads: selected in one workgroup's LDS
     st = lib.lh_forward(ctypes.byref(shape), 1, 1, 1, 1, None, 1, z.ws_forward, None)
     assert st == 1 and b"buffers" in lib.lh_last_error()
 

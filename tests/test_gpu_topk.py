@@ -1,6 +1,7 @@
 """GPU parity of lh_topk on score arrays the parity workloads do not produce:
-candidate counts whose histogram blocks cover several slices with a partial
-last block, many exact ties at the threshold (the cut falls inside a run of
+heads small enough for the single-workgroup path (up to 16384 candidates)
+and just above it, candidate counts whose histogram blocks cover several
+slices with a partial last block, many exact ties at the threshold (the cut falls inside a run of
 equal scores that spans slices), every candidate tied, K = 1, K = C, and a
 head whose scores decrease with the flat index (the K selected candidates are
 the first K).
@@ -57,6 +58,13 @@ CASES = [
     ("k_one", 65536, 64, 4, 4, 1, ("norms", "few_values")),
     ("k_all", 65536, 64, 4, 4, None, ("norms",)),
     ("decreasing", 131072, 64, 2, 5, 30000, ("decreasing",)),
+    # heads of at most 16384 candidates: selected in one workgroup's LDS
+    ("small_max", 16384, 64, 2, 2, 3000, ("norms", "few_values")),      # C = 16384 exactly
+    ("small_all_equal", 4096, 64, 4, 3, 777, ("all_equal",)),
+    ("small_k_one", 8192, 64, 2, 2, 1, ("few_values", "norms", "decreasing")),
+    ("small_k_all", 12288, 64, 4, 2, None, ("few_values",)),
+    # just above: the multi-kernel path with 5 slices, the last holding 2 candidates
+    ("large_min", 16386, 64, 2, 2, 9000, ("few_values", "norms")),
 ]
 
 
