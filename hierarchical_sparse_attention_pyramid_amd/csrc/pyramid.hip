@@ -309,19 +309,19 @@ __global__ __launch_bounds__(256) void pool_bwd_kernel(PoolBwdArgs a) {
   for (int rb = 0; rb < nrows; rb += kRowsInFlight) {
     float xs[kRowsInFlight][8];
     int32_t pt[kRowsInFlight];
+    bool inside[kRowsInFlight];  // causal: the virtual row is a token
 #pragma unroll
     for (int u = 0; u < kRowsInFlight; ++u) {
       const int64_t row = r0 + min(rb + u, nrows - 1);
       if constexpr (FIRST && SH != 0) {
-        // token row of virtual row `row`: zeros before the first token and in the padding
+        // token row of virtual row `row`, clamped into the tokens so that the
+        // load needs no branch; rows outside get weight 0 below
         const int64_t t = row - SH;
-        if (t >= 0 && t < g.N) {
-          Row8<Tin>::template load<kStream>(in + t * a.lin.sn, xs[u]);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) xs[u][e] = 0.f;
-        }
+        inside[u] = t >= 0 && t < g.N;
+        const int64_t tc = t < 0 ? 0 : (t < g.N ? t : g.N - 1);
+        Row8<Tin>::template load<kStream>(in + tc * a.lin.sn, xs[u]);
       } else {
+        inside[u] = true;
         Row8<Tin>::template load<kStream>(in + row * a.lin.sn, xs[u]);
       }
       if constexpr (FIRST) pt[u] = sp[row - B0];
@@ -341,8 +341,10 @@ __global__ __launch_bounds__(256) void pool_bwd_kernel(PoolBwdArgs a) {
           walk.advance((int32_t)row, posf, nullptr, g, true, lane);
           ct += walk.cnt[1];
         }
-        // span reading: every token has a contributor; causal: 0 for an unfed token
-        const float rc = SH == 0 || ct > 0 ? 1.0f / static_cast<float>(ct) : 0.0f;
+        // span reading: every token has a contributor; causal: 0 for an unfed
+        // token and for the virtual rows that are no token
+        const float rc =
+            SH == 0 || (ct > 0 && inside[u]) ? 1.0f / static_cast<float>(ct) : 0.0f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) xs[u][e] *= rc;
         if (pt[u] >= 0) Row8<Tout>::store(dos + (int64_t)pt[u] * d, xs[u]);

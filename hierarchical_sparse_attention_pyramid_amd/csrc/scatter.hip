@@ -114,16 +114,18 @@ __global__ __launch_bounds__(256) void bcast_kernel(BcastArgs a) {
     for (int u = 0; u < kU; ++u) {
       if (t + u >= t1) break;
       w.advance(t + u, vpos, src, g, mean, lane);
-      if (SH != 0 && t + u < SH) continue;  // virtual token 0 of the causal reading: no output row
       const int c = w.cnt[1] + (r0[u] >= 0 ? 1 : 0);
       // span reading: every token has a contributor; causal: 0 for an unfed token
       const float rc = mean ? (SH == 0 || c > 0 ? 1.0f / static_cast<float>(c) : 0.0f) : 1.0f;
+      // causal: virtual token 0 (no token) writes zeros to row 0, which the
+      // same lanes' next store (token 0) overwrites; no branch per token
+      const int32_t row = SH == 0 ? t + u : max(t + u - SH, 0);
 #pragma unroll
       for (int i = 0; i < NT; ++i) {
         float o[kE];
 #pragma unroll
         for (int e = 0; e < kE; ++e) o[e] = (w.A[1][i][e] + v0[u][i][e]) * rc;
-        Out4<Tout>::store(out[i] + (int64_t)(t + u - SH) * a.lout.sn, o);
+        Out4<Tout>::store(out[i] + (int64_t)row * a.lout.sn, o);
       }
     }
   }
@@ -300,7 +302,6 @@ __global__ __launch_bounds__(256) void bcast_fast(BcastArgs a) {
     for (int u = 0; u < kFastU; ++u) {
       const int32_t t = c + u;
       if (t >= t1) break;
-      if (SH != 0 && t < SH) continue;  // virtual token 0 of the causal reading: no output row
       const int cnt = C[0] + b.s0[u];
       // span reading: every token has a contributor; causal: 0 for an unfed token
       const float rc =
@@ -308,7 +309,9 @@ __global__ __launch_bounds__(256) void bcast_fast(BcastArgs a) {
       float o[kE];
 #pragma unroll
       for (int e = 0; e < kE; ++e) o[e] = (A[0][e] + b.r0[u][e]) * rc;
-      Out4<Tout>::store(out + (int64_t)(t - SH) * a.lout.sn, o);
+      // causal: virtual token 0 (no token) writes zeros to row 0, which the
+      // same lanes' next store (token 0) overwrites; no branch per token
+      Out4<Tout>::store(out + (int64_t)(SH == 0 ? t : max(t - SH, 0)) * a.lout.sn, o);
     }
   };
   if (nin == 0) {  // A[0] must be the outer sum
