@@ -7,6 +7,7 @@ torch is used to allocate device memory in the `alloc_*` helpers.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 
@@ -273,6 +274,16 @@ class LayerBuffers:
         return Buffers(*(p(getattr(self, f)) for f in self.FIELDS))
 
 
+def _on_stream(stream):
+    """Context making `stream` (a torch stream or a raw hipStream_t handle)
+    torch's current stream; a no-op for None."""
+    if stream is None:
+        return contextlib.nullcontext()
+    if not isinstance(stream, torch.cuda.Stream):
+        stream = torch.cuda.ExternalStream(int(getattr(stream, "cuda_stream", stream)))
+    return torch.cuda.stream(stream)
+
+
 def workspace(nbytes: int, device="cuda") -> torch.Tensor | None:
     return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device) if nbytes else None
 
@@ -285,7 +296,16 @@ def forward(q, k, v, p: int, L: int, S: int, out=None, stream=None, scatter="spa
     contiguous), e.g. slices of a packed projection; otherwise they are made
     contiguous.  `out`, if given, is a [B,H,N,d] view to write into (any
     layout with a contiguous last dimension); else a packed tensor is
-    allocated."""
+    allocated.
+
+    With `stream` given, every allocation (out, buffers, workspace, contiguous
+    copies) and the launch happen on that stream, so the caching allocator
+    reuses the workspace only after the stream's kernels."""
+    with _on_stream(stream):
+        return _forward(q, k, v, p, L, S, out, scatter)
+
+
+def _forward(q, k, v, p, L, S, out, scatter):
     B, H, N, d = q.shape
     st = token_strides(q, k, v)
     if st is None:
@@ -299,14 +319,20 @@ def forward(q, k, v, p: int, L: int, S: int, out=None, stream=None, scatter="spa
     shape = make_shape(B, H, N, d, p, L, S, q.dtype, st, ost, scatter)
     bufs = LayerBuffers(shape, q.device)
     ws = workspace(bufs.sizes.ws_forward, q.device)
-    lh_forward(shape, q, k, v, out, bufs, ws, stream)
+    lh_forward(shape, q, k, v, out, bufs, ws)
     return out, bufs, shape
 
 
 def backward(shape, dout, bufs: LayerBuffers, dq=None, dk=None, dv=None, stream=None):
     """dq, dk, dv of the forward that filled `bufs`.  dout: any [B,H,N,d]
     layout with a contiguous last dimension (else made contiguous); dq, dk,
-    dv: views sharing one layout to write into, or None for packed tensors."""
+    dv: views sharing one layout to write into, or None for packed tensors.
+    `stream` as in forward()."""
+    with _on_stream(stream):
+        return _backward(shape, dout, bufs, dq, dk, dv)
+
+
+def _backward(shape, dout, bufs, dq, dk, dv):
     if token_strides(dout) is None:
         dout = dout.contiguous()
     if dq is None:
@@ -317,5 +343,5 @@ def backward(shape, dout, bufs: LayerBuffers, dq=None, dk=None, dv=None, stream=
         raise ValueError("dq, dk, dv must be [B,H,N,d] views sharing one layout")
     call_shape = with_strides(shape, gst, token_strides(dout))
     ws = workspace(bufs.sizes.ws_backward, dout.device)
-    lh_backward(call_shape, dout, bufs, dq, dk, dv, ws, stream)
+    lh_backward(call_shape, dout, bufs, dq, dk, dv, ws)
     return dq, dk, dv

@@ -58,3 +58,27 @@ def test_graph_replays_match_eager(name, gpu_lib):
             assert torch.equal(a, b), f"replay {rep}: {key} differs from the eager step"
         step()  # eager work between replays
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("kind", ["torch_stream", "raw_handle"])
+def test_helpers_on_a_side_stream(kind, gpu_lib):
+    """binding.forward / backward with an explicit stream: allocations and
+    launches go to that stream and the results equal the default stream's."""
+    lb = gpu_lib
+    case = next(c for c in CASES if c[0] == "d128_ragged_bf16")
+    R = run_case(case)
+    _, B, H, N, d, p, L, S, dt = case
+    print(f"[stream] {kind}", flush=True)
+    q, k, v, dout = (to_device(R["host"][t], dt) for t in ("q", "k", "v", "dout"))
+    ref_out, ref_bufs, ref_shape = lb.forward(q, k, v, p, L, S)
+    ref = (ref_out, *lb.backward(ref_shape, dout, ref_bufs))
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    handle = side if kind == "torch_stream" else side.cuda_stream
+    side.wait_stream(torch.cuda.current_stream())
+    for _ in range(2):  # the second call reuses the first call's freed workspace
+        out, bufs, shape = lb.forward(q, k, v, p, L, S, stream=handle)
+        got = (out, *lb.backward(shape, dout, bufs, stream=handle))
+    side.synchronize()
+    for g, r in zip(got, ref):
+        assert torch.equal(g, r)
