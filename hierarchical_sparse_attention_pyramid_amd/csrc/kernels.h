@@ -25,11 +25,12 @@ struct PoolFwdArgs {
   int32_t lvl0;          // level of the input rows
   int32_t lam;           // levels produced: lvl0+1 .. lvl0+lam
   int32_t chunk;         // input rows per row group (a multiple of p^lam)
-  // token pass only: words [zero_off, zero_off + zero_words) of each of
-  // zero_heads heads, zero_stride words apart from `zero`, are cleared (the
-  // top-K histograms of lh_forward); null: nothing
-  uint32_t* zero;
-  int64_t zero_heads, zero_stride, zero_off, zero_words;
+  // the large-head top-K's workspace (hist_stride words per head): every
+  // candidate score written (flat index below C) is counted into its pass-0
+  // histograms (hist0.h), which must be zero when the first pass starts;
+  // null: no counting
+  uint32_t* hist;
+  int64_t hist_stride;
   Geo g;
 };
 
@@ -63,17 +64,17 @@ hipError_t launch_bcast(const BcastArgs& a, int dtype, int ntensors, int64_t BH,
 
 // top-K
 // Heads of at most 16384 candidates are selected in one workgroup's LDS (no
-// workspace); larger ones use a workspace whose words [off, off + words) of
-// each head (stride words apart) must be zero before the selection runs.
-struct TopkZero {
-  int64_t stride, off, words;  // uint32 words; all zero: nothing to clear
-};
+// workspace); larger ones use a workspace of topk_hist_stride(C) words per
+// head, whose pass-0 histograms (hist0.h) start each selection at zero.
 bool topk_small_path(int64_t C);
 size_t topk_ws_bytes(int64_t BH, int64_t C);
-TopkZero topk_zero_region(int64_t C);
-// zeroed: the caller already cleared the region (else a clearing kernel runs first)
+int64_t topk_hist_stride(int64_t C);  // 0 on the small path
+// clears the histograms (large heads; nothing on the small path)
+hipError_t launch_topk_zero(void* ws, int64_t C, int64_t BH, hipStream_t st);
+// counted: the caller cleared the histograms and counted pass 0 (the pooling
+// kernel in lh_forward); else the clearing kernel and the pass-0 kernel run first
 hipError_t launch_topk(const float* score, int32_t* sel, void* ws, const Geo& g, int64_t BH,
-                       bool zeroed, hipStream_t st);
+                       bool counted, hipStream_t st);
 
 // gather
 // q, k, v: token tensors of layout lq

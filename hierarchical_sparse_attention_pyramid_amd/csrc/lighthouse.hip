@@ -292,15 +292,9 @@ lh_status run_pool(const Plan& P, const void* q, const void* k, const void* v, v
     a.lvl0 = t.lvl0;
     a.lam = t.lam;
     a.chunk = t.chunk;
-    if (s == 0 && topk_ws != nullptr) {  // the top-K's histograms start at zero
-      const lh::TopkZero zr = lh::topk_zero_region(P.g.C);
-      if (zr.words > 0) {
-        a.zero = static_cast<uint32_t*>(topk_ws);
-        a.zero_heads = P.BH;
-        a.zero_stride = zr.stride;
-        a.zero_off = zr.off;
-        a.zero_words = zr.words;
-      }
+    if (do_score && topk_ws != nullptr) {  // count the candidates for the top-K
+      a.hist = static_cast<uint32_t*>(topk_ws);
+      a.hist_stride = lh::topk_hist_stride(P.g.C);
     }
     a.g = P.g;
     LH_HIP(lh::launch_pool_fwd(a, P.dtype, P.BH, s == 0, do_pool, do_score, st), "pyramid");
@@ -509,13 +503,17 @@ static lh_status check_forward_args(const Plan& P, const void* q, const void* k,
 static lh_status run_forward(const Plan& P, const void* q, const void* k, const void* v, void* out,
                              const lh_buffers* b, void* ws, hipStream_t st, hipEvent_t* ev) {
   lh_status s;
-  // the top-K region follows the pooling sums; the pooling pass clears it
-  void* tws = P.g.K > 0 ? static_cast<char*>(ws) + align_up(P.sz.ws_build_pyramid) : nullptr;
+  // The top-K region follows the pooling sums.  For heads above the
+  // small-path size its pass-0 histograms are cleared first and the pooling
+  // kernels count the candidate scores into them as they write them.
+  const bool counted = P.g.K > 0 && !lh::topk_small_path(P.g.C);
+  void* tws = counted ? static_cast<char*>(ws) + align_up(P.sz.ws_build_pyramid) : nullptr;
+  if (counted) LH_HIP(lh::launch_topk_zero(tws, P.g.C, P.BH, st), "topk");
   if ((s = run_pool(P, q, k, v, b->pq, b->pk, b->pv, b->score, ws, P.g.L > 1, true, st, tws)) !=
       LH_OK)
     return s;
   if (ev) LH_HIP(hipEventRecord(ev[0], st), "event");
-  LH_HIP(lh::launch_topk(b->score, b->sel, tws, P.g, P.BH, true, st), "topk");
+  LH_HIP(lh::launch_topk(b->score, b->sel, tws, P.g, P.BH, counted, st), "topk");
   if (ev) LH_HIP(hipEventRecord(ev[1], st), "event");
   const void* lv0[3] = {q, k, v};
   const void* pyr[3] = {b->pq, b->pk, b->pv};

@@ -14,6 +14,7 @@
 // input row is read exactly once and every level is produced in the same
 // pass.  Deep pyramids use several passes: a pass hands the float32 sums of
 // its top level to the next one.
+#include "hist0.h"
 #include "kernels.h"
 #include "walk.h"
 
@@ -66,13 +67,19 @@ __device__ __forceinline__ float row_norm(const float (&x)[8], int lpr) {
   return sqrtf(c0 + c1);  // correctly rounded on gfx950 (not __fsqrt_rn)
 }
 
+// Candidate scores one row group stages for the top-K's counting: its chunk
+// (at most 64 rows) and the coarser entries completed in it.
+constexpr int kStageCap = 128;
+
 // One pass over the tensors listed in `tid` for the chunk of rows
 // [r0, r0 + nrows) of head bh.  SCORE: 0 none, 1 norms (level 0 input),
-// 2 max-pool of stored level-lvl0 scores.
+// 2 max-pool of stored level-lvl0 scores.  stage (LDS, kStageCap words, or
+// null): the row group's list of candidate score bits written, nst their
+// count; they are counted after the pass, off the row loop.
 template <typename Tin, typename Tout, int NT, int SCORE>
 __device__ __forceinline__ void pool_pass(const PoolFwdArgs& a, const int (&tid)[NT],
                                           bool do_pool, int64_t bh, int64_t r0, int nrows,
-                                          int lane) {
+                                          int lane, uint32_t* stage, int& nst) {
   const Geo& g = a.g;
   const int d = g.d;
   const int lpr = d / 8;
@@ -126,7 +133,10 @@ __device__ __forceinline__ void pool_pass(const PoolFwdArgs& a, const int (&tid)
       float s = 0.f;
       if constexpr (SCORE == 1) {
         s = row_norm(xs[u][0], lpr) + row_norm(xs[u][1], lpr);
-        if (lane == 0) score[row] = s;
+        if (lane == 0) {
+          score[row] = s;
+          if (stage != nullptr && row < g.C && nst < kStageCap) stage[nst++] = __float_as_uint(s);
+        }
       } else if constexpr (SCORE == 2) {
         s = sin[u];
       }
@@ -155,7 +165,12 @@ __device__ __forceinline__ void pool_pass(const PoolFwdArgs& a, const int (&tid)
           }
         }
         if constexpr (SCORE != 0) {
-          if (lane == 0) score[g.base[lev] + j] = smax[l];
+          if (lane == 0) {
+            const int64_t flat = g.base[lev] + j;
+            score[flat] = smax[l];
+            if (stage != nullptr && flat < g.C && nst < kStageCap)
+              stage[nst++] = __float_as_uint(smax[l]);
+          }
         }
         if (l + 1 < kStageLevels && l + 1 < a.lam) {
           if (do_pool) {
@@ -182,40 +197,49 @@ __device__ __forceinline__ void pool_pass(const PoolFwdArgs& a, const int (&tid)
 
 template <typename Tin, typename Tout, bool FIRST>
 __global__ __launch_bounds__(256) void pool_fwd_kernel(PoolFwdArgs a, int do_pool, int do_score) {
-  if (FIRST && a.zero != nullptr) {
-    // clear a region for a later kernel of the same call (16-byte stores,
-    // spread over every workgroup of the grid)
-    const int64_t per = a.zero_words / 4;
-    const int64_t total = a.zero_heads * per;
-    const int64_t nthreads = (int64_t)gridDim.x * gridDim.y * blockDim.x;
-    for (int64_t i = ((int64_t)blockIdx.y * gridDim.x + blockIdx.x) * blockDim.x + threadIdx.x;
-         i < total; i += nthreads) {
-      const int64_t h = i / per;
-      reinterpret_cast<uint4*>(a.zero + h * a.zero_stride + a.zero_off)[i - h * per] =
-          make_uint4(0u, 0u, 0u, 0u);
-    }
-  }
+  // the top-K's pass-0 counting (hist0.h) of the candidate scores written:
+  // each row group lists them in LDS, and the workgroup counts the lists
+  // after the row walk
+  __shared__ Hist0Lds hl;
+  __shared__ uint32_t stage[32 * kStageCap];
+  __shared__ int nstage[32];
+  const bool count = a.hist != nullptr && do_score;  // uniform
   const int lpr = a.g.d / 8;
   const int rgs = 256 / lpr;
   const int rg = threadIdx.x / lpr, lane = threadIdx.x % lpr;
   const int64_t bh = blockIdx.y;
+  int nst = 0;
+  if (count) hist0_init(hl);
   const int64_t nchunks = (a.in_rows + a.chunk - 1) / a.chunk;
   const int64_t c = (int64_t)blockIdx.x * rgs + rg;
-  if (c >= nchunks) return;  // no block-wide barrier in this kernel
-  const int64_t r0 = c * a.chunk;
-  const int nrows = (int)min((int64_t)a.chunk, a.in_rows - r0);
-  constexpr int kScore = FIRST ? 1 : 2;
-  // pass 1: q and k (with the scores); pass 2: v (two passes keep fewer
-  // rows' accumulators live in registers than one pass over all three)
-  const int qk[2] = {0, 1};
-  if (do_score) {
-    pool_pass<Tin, Tout, 2, kScore>(a, qk, do_pool != 0, bh, r0, nrows, lane);
-  } else if (do_pool) {
-    pool_pass<Tin, Tout, 2, 0>(a, qk, true, bh, r0, nrows, lane);
+  if (c < nchunks) {
+    const int64_t r0 = c * a.chunk;
+    const int nrows = (int)min((int64_t)a.chunk, a.in_rows - r0);
+    constexpr int kScore = FIRST ? 1 : 2;
+    // pass 1: q and k (with the scores); pass 2: v (two passes keep fewer
+    // rows' accumulators live in registers than one pass over all three)
+    const int qk[2] = {0, 1};
+    if (do_score) {
+      pool_pass<Tin, Tout, 2, kScore>(a, qk, do_pool != 0, bh, r0, nrows, lane,
+                                      count ? stage + rg * kStageCap : nullptr, nst);
+    } else if (do_pool) {
+      pool_pass<Tin, Tout, 2, 0>(a, qk, true, bh, r0, nrows, lane, nullptr, nst);
+    }
+    if (do_pool) {
+      const int vv[1] = {2};
+      pool_pass<Tin, Tout, 1, 0>(a, vv, true, bh, r0, nrows, lane, nullptr, nst);
+    }
   }
-  if (do_pool) {
-    const int vv[1] = {2};
-    pool_pass<Tin, Tout, 1, 0>(a, vv, true, bh, r0, nrows, lane);
+  if (count) {  // every thread of the workgroup reaches these barriers
+    if (lane == 0) nstage[rg] = nst;
+    __syncthreads();
+    uint32_t* hw = a.hist + bh * a.hist_stride;
+    for (int i = threadIdx.x; i < rgs * kStageCap; i += 256) {
+      const int r = i / kStageCap, j = i % kStageCap;
+      if (j < nstage[r]) hist0_add(hl, stage[i], hw);
+    }
+    __syncthreads();
+    hist0_flush(hl, hw);
   }
 }
 

@@ -36,9 +36,10 @@
 //          counts the candidates its earlier slices select from the
 //          records alone (the slices' totals above P0, E, and those few
 //          entries), and compacts its own slices in flat order.
-//    The global histograms start each call at zero: in lh_forward the
-//    pooling kernel clears them (it runs first); lh_topk launches a small
-//    clearing kernel of its own.
+//    The global histograms start each call at zero (a small clearing
+//    kernel).  In lh_forward the pooling kernel that writes the scores also
+//    does h0's counting (hist0.h), so the top-K stage itself is h1 and w.
+#include "hist0.h"
 #include "kernels.h"
 
 namespace lh {
@@ -64,9 +65,10 @@ constexpr int kMaxSub = 15;               // slices per h0 workgroup: its LDS co
 //       +2 E[256] (uint16): entries whose bits 15..8 exceed b start at E[b],
 //       +130 entries[4096] (uint16): low 16 bits, grouped by bits 15..8, descending.
 // Words [kHdr, kZeroEnd) must be zero when h0 starts.
-constexpr int kHdr = 8;
-constexpr int kC0 = kHdr;
-constexpr int kF0 = kC0 + 256;
+constexpr int kHdr = kTopkC0;
+constexpr int kC0 = kTopkC0;
+constexpr int kF0 = kTopkF0;
+static_assert(kF0 == kC0 + 256, "pass-0 histogram layout");
 constexpr int kC1 = kF0 + 65536;
 constexpr int kZeroEnd = kC1 + 256;
 constexpr int kSliceBase = (kZeroEnd + 63) / 64 * 64;
@@ -234,23 +236,11 @@ __global__ __launch_bounds__(kThreads) void topk_zero(void* ws, int64_t stride) 
     z[i] = make_uint4(0u, 0u, 0u, 0u);
 }
 
-// Pass 0: histogram of bits 31..16 over slices [s0, s1) of one head.  The
-// LDS table is direct-mapped: coarse bin c (score bits 31..24) counts in slot
-// c % kSlots, which the first candidate of that bin claims with a
-// compare-and-swap of the slot's tag; a candidate whose slot another coarse
-// bin holds goes straight to the global histograms.  Scores of one layer span
-// a few adjacent coarse bins, so collisions do not occur in practice, and the
-// slice loop needs no barrier.  The flush adds each pair of adjacent fine
-// bins with one 64-bit atomic (the global fine histogram is read as 32-bit
-// counts; a pair's low count never carries into the high one).
-constexpr int kSlots = 16;
-constexpr uint32_t kFree = 0xFFFFFFFFu;
-
+// Pass 0: histogram of bits 31..16 over slices [s0, s1) of one head, in the
+// LDS table of hist0.h (the slice loop needs no barrier).
 __global__ __launch_bounds__(kThreads) void topk_h0(const float* score, void* ws, int64_t stride,
                                                     int32_t M, int32_t C, int32_t nsl, int32_t nsub) {
-  __shared__ uint32_t lf[kSlots * 128];  // bin f of slot k: half f & 1 of word k*128 + (f & 255) / 2
-  __shared__ uint32_t tag[kSlots];       // coarse bin counted in each slot, or kFree
-  __shared__ uint32_t lc[kSlots];        // per slot totals
+  __shared__ Hist0Lds hl;
   const int64_t bh = blockIdx.y;
   uint32_t* w = head_ws(ws, bh, stride);
   const float* s = score + bh * M;
@@ -258,12 +248,7 @@ __global__ __launch_bounds__(kThreads) void topk_h0(const float* score, void* ws
   const int s0 = blockIdx.x * nsub, s1 = min(s0 + nsub, nsl);
   uint32_t u[kPer];
   if (s0 < s1) load_slice(s, s0 * kSlice, C, u);
-  for (int i = t; i < kSlots * 32; i += kThreads)
-    reinterpret_cast<uint4*>(lf)[i] = make_uint4(0u, 0u, 0u, 0u);
-  if (t < kSlots) {
-    tag[t] = kFree;
-    lc[t] = 0u;
-  }
+  hist0_init(hl);
   __syncthreads();
   for (int sl = s0; sl < s1; ++sl) {
     const int i0 = sl * kSlice;
@@ -271,42 +256,15 @@ __global__ __launch_bounds__(kThreads) void topk_h0(const float* score, void* ws
     const bool more = sl + 1 < s1;
     if (more) load_slice(s, (sl + 1) * kSlice, C, nx);
 #pragma unroll
-    for (int r = 0; r < kPer; ++r) {
-      if (i0 + r * kThreads + t < C) {
-        const uint32_t f = u[r] >> 16, c = f >> 8, k = c % kSlots;
-        uint32_t tg = tag[k];
-        if (tg == kFree) {
-          const uint32_t old = atomicCAS(&tag[k], kFree, c);
-          tg = old == kFree ? c : old;
-        }
-        if (tg == c) {
-          atomicAdd(&lf[k * 128 + ((f & 255u) >> 1)], (f & 1u) ? 0x10000u : 1u);
-        } else {  // the slot holds another coarse bin: straight to the global histograms
-          atomicAdd(&w[kF0 + f], 1u);
-          atomicAdd(&w[kC0 + c], 1u);
-        }
-      }
-    }
+    for (int r = 0; r < kPer; ++r)
+      if (i0 + r * kThreads + t < C) hist0_add(hl, u[r], w);
     if (more) {
 #pragma unroll
       for (int r = 0; r < kPer; ++r) u[r] = nx[r];
     }
   }
   __syncthreads();
-  // flush the claimed slots
-  for (int i = t; i < kSlots * 128; i += kThreads) {
-    const int k = i >> 7;
-    const uint32_t v = lf[i];
-    if (v) {
-      const uint32_t lo = v & 0xFFFFu, hi = v >> 16;
-      const uint32_t f = (tag[k] << 8) | ((uint32_t)(i & 127) << 1);
-      atomicAdd(reinterpret_cast<unsigned long long*>(w + kF0 + f),
-                ((unsigned long long)hi << 32) | lo);
-      atomicAdd(&lc[k], lo + hi);
-    }
-  }
-  __syncthreads();
-  if (t < kSlots && lc[t]) atomicAdd(&w[kC0 + tag[t]], lc[t]);
+  hist0_flush(hl, w);
 }
 
 // Pick of pass 0, then the per-slice records and the pass-1 coarse histogram.
@@ -513,13 +471,16 @@ size_t topk_ws_bytes(int64_t BH, int64_t C) {
   return topk_small_path(C) ? 0 : (size_t)BH * (size_t)head_stride(C) * sizeof(uint32_t);
 }
 
-TopkZero topk_zero_region(int64_t C) {
-  if (topk_small_path(C)) return TopkZero{0, 0, 0};
-  return TopkZero{head_stride(C), kHdr, kZeroEnd - kHdr};
+int64_t topk_hist_stride(int64_t C) { return topk_small_path(C) ? 0 : head_stride(C); }
+
+hipError_t launch_topk_zero(void* ws, int64_t C, int64_t BH, hipStream_t st) {
+  if (topk_small_path(C)) return hipSuccess;
+  topk_zero<<<dim3(16, (unsigned)BH), kThreads, 0, st>>>(ws, head_stride(C));
+  return hipGetLastError();
 }
 
 hipError_t launch_topk(const float* score, int32_t* sel, void* ws, const Geo& g, int64_t BH,
-                       bool zeroed, hipStream_t st) {
+                       bool counted, hipStream_t st) {
   if (g.K == 0) return hipSuccess;
   if (topk_small_path(g.C)) {
     topk_small<<<(unsigned)BH, kSmallThreads, 0, st>>>(score, sel, g.M, g.C, g.K);
@@ -527,15 +488,18 @@ hipError_t launch_topk(const float* score, int32_t* sel, void* ws, const Geo& g,
   }
   const int64_t stride = head_stride(g.C);
   const int64_t nsl = nslices(g.C);
-  if (!zeroed) topk_zero<<<dim3(16, (unsigned)BH), kThreads, 0, st>>>(ws, stride);
   // workgroups of one slice each, up to about LH_TOPK_WG in all (the
   // kernels are bound by per-slice latency, not bandwidth); h0 takes at most
   // kMaxSub slices per workgroup (16-bit LDS counters)
   const int64_t want = std::max<int64_t>(1, (LH_TOPK_WG + BH - 1) / BH);
-  const int64_t hb0 = std::min<int64_t>(nsl, std::max<int64_t>(want, (nsl + kMaxSub - 1) / kMaxSub));
-  const int64_t nsub0 = (nsl + hb0 - 1) / hb0;
-  topk_h0<<<dim3((unsigned)((nsl + nsub0 - 1) / nsub0), (unsigned)BH), kThreads, 0, st>>>(
-      score, ws, stride, g.M, g.C, (int32_t)nsl, (int32_t)nsub0);
+  if (!counted) {
+    topk_zero<<<dim3(16, (unsigned)BH), kThreads, 0, st>>>(ws, stride);
+    const int64_t hb0 =
+        std::min<int64_t>(nsl, std::max<int64_t>(want, (nsl + kMaxSub - 1) / kMaxSub));
+    const int64_t nsub0 = (nsl + hb0 - 1) / hb0;
+    topk_h0<<<dim3((unsigned)((nsl + nsub0 - 1) / nsub0), (unsigned)BH), kThreads, 0, st>>>(
+        score, ws, stride, g.M, g.C, (int32_t)nsl, (int32_t)nsub0);
+  }
   const int64_t hb1 = std::min<int64_t>(nsl, want);
   const int64_t nsub1 = (nsl + hb1 - 1) / hb1;
   topk_h1<<<dim3((unsigned)((nsl + nsub1 - 1) / nsub1), (unsigned)BH), kThreads, 0, st>>>(

@@ -40,6 +40,9 @@ CASES = [
     ("p64_bf16", 1, 2, 8192, 64, 64, 3, 400, "bf16"),         # largest pooling factor
     ("deep_L16_fp32", 1, 1, 32768, 64, 2, 16, 300, "fp32"),   # deepest pyramid (one coarse entry)
     ("zeros_bf16", 1, 2, 1024, 64, 4, 4, 200, "bf16"),        # all-zero q, k, v: every score tied
+    # above 16384 candidates per head the pooling kernel counts the top-K's
+    # first histogram pass; repeated rows tie scores across its slices
+    ("ties_n32k_bf16", 1, 2, 32768, 64, 4, 3, 3000, "bf16"),
 ]
 ids = [c[0] for c in CASES]
 _cache: dict = {}

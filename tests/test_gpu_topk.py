@@ -92,3 +92,44 @@ def test_topk_matches_oracle(case, gpu_lib):
     for h in range(H):
         want = O.topk(score[0, h], N, p, L, S)
         np.testing.assert_array_equal(g_sel[0, h].cpu().numpy(), want, err_msg=f"{name} head {h}")
+
+
+# lh_forward on heads above 16384 candidates: the pooling kernels count the
+# first histogram pass as they write the scores (the top-K stage runs only
+# its later passes).  name, N, d, p, L, S, row-scale exponent range, tie blocks
+FWD_CASES = [
+    # row scales 2^-24..2^24: the scores span more coarse bins (top 8 bits)
+    # than the counting table has slots, so some go to the global fallback
+    ("fwd_wide", 16384, 64, 4, 4, 2000, 24, 1),
+    # p = 2, L = 6: level-4 candidates are counted by the second pooling pass
+    ("fwd_upper_pass", 16384, 64, 2, 6, 3000, 0, 1),
+    # repeated rows: long runs of equal scores around the threshold
+    ("fwd_ties", 32768, 128, 4, 3, 3000, 0, 16),
+]
+
+
+@pytest.mark.parametrize("case", FWD_CASES, ids=[c[0] for c in FWD_CASES])
+def test_forward_counted_selection(case, gpu_lib):
+    from synth import inputs as synth
+    lb = gpu_lib
+    name, N, d, p, L, S, span, rep = case
+    H = 2
+    print(f"[topk-fwd] case {name}: N={N} d={d} p={p} L={L} S={S}", flush=True)
+    e = np.random.default_rng(61 + FWD_CASES.index(case)).integers(-span, span + 1, size=N)
+    scale = np.exp2(e).astype(np.float32)[:, None]
+    host = {}
+    for t in ("q", "k", "v"):
+        rows = [synth.head_tensor(80 + FWD_CASES.index(case), t, 0, h, N, d) for h in range(H)]
+        rows = [np.repeat(x[::rep], rep, axis=0) * scale for x in rows]
+        host[t] = synth.bf16_bits_from_f32(np.stack(rows)[None])
+    dev = {t: torch.from_numpy(host[t].view(np.int16)).view(torch.bfloat16).cuda() for t in host}
+    out, bufs, shape = lb.forward(dev["q"], dev["k"], dev["v"], p, L, S)
+    torch.cuda.synchronize()
+    assert bufs.sizes.C > 16384
+    for h in range(H):
+        want = O.select_head(host["q"][0, h], host["k"][0, h], p, L, S, "bf16")
+        got_score = bufs.score[0, h].cpu().numpy()
+        assert np.array_equal(got_score.view(np.uint32), want["score"].view(np.uint32)), name
+        for key in ("sel", "sub_idx", "pos"):
+            np.testing.assert_array_equal(getattr(bufs, key)[0, h].cpu().numpy(), want[key],
+                                          err_msg=f"{name} head {h} {key}")
