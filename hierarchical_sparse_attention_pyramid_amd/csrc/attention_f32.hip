@@ -39,14 +39,23 @@ __device__ __forceinline__ void stage(float* dst, const float* src, int S, int r
   }
 }
 
+// Forward: a query's keys are split over kSplit lane groups (key j of a tile
+// goes to group j mod kSplit), each with its own running max, normaliser and
+// output; the groups of a query sit 4 lanes apart in one wave and are merged
+// with butterfly shuffles at the end.  Splitting the keys gives a workgroup
+// 256 / (4 kSplit) queries, so short sequences still spread over many
+// workgroups and each lane's dependent chain is kSplit times shorter.
+constexpr int kSplit = 16;
+
 template <int D>
 __global__ __launch_bounds__(256) void attn_fwd_f32(const float* __restrict__ Q, const float* __restrict__ K,
                                                     const float* __restrict__ V, float* __restrict__ O,
                                                     float* __restrict__ LSE, int S, double scale) {
+  constexpr int kQ = 256 / (4 * kSplit);  // queries per workgroup
   __shared__ float sK[kRows * D], sV[kRows * D];
-  const int tid = threadIdx.x, sub = tid & 3;
+  const int tid = threadIdx.x, sub = tid & 3, grp = (tid >> 2) % kSplit;
   const int64_t off = blockIdx.y * (int64_t)S * D;
-  const int query = blockIdx.x * kRows + tid / 4;
+  const int query = blockIdx.x * kQ + tid / (4 * kSplit);
   float q[D / 4];
   double o[D / 4];
 #pragma unroll
@@ -55,13 +64,14 @@ __global__ __launch_bounds__(256) void attn_fwd_f32(const float* __restrict__ Q,
     o[e] = 0.0;
   }
   double m = -1e300, l = 0.0;
-  const int kend = min(S, (int)(blockIdx.x + 1) * kRows);
+  const int kend = min(S, (int)(blockIdx.x + 1) * kQ);
   for (int k0 = 0; k0 < kend; k0 += kRows) {
     __syncthreads();
     stage<D>(sK, K + off, S, k0, tid);
     stage<D>(sV, V + off, S, k0, tid);
     __syncthreads();
-    for (int j = 0; j < kRows; ++j) {
+    for (int jj = 0; jj < kRows / kSplit; ++jj) {
+      const int j = jj * kSplit + grp;
       const double s = dot4<D>(q, sK + j * D + sub * (D / 4)) * scale;
       if (k0 + j > query) continue;
       const double mn = fmax(m, s);
@@ -73,7 +83,19 @@ __global__ __launch_bounds__(256) void attn_fwd_f32(const float* __restrict__ Q,
       m = mn;
     }
   }
-  if (query >= S) return;
+  // merge the key groups of each query (lanes 4, 8, 16, 32 apart); a group that
+  // saw no key has l = 0 and o = 0, and its weight underflows to 0
+#pragma unroll
+  for (int w = 4; w < 4 * kSplit; w <<= 1) {
+    const double mo = __shfl_xor(m, w), lo = __shfl_xor(l, w);
+    const double mn = fmax(m, mo);
+    const double a = expf((float)(m - mn)), b = expf((float)(mo - mn));
+    l = l * a + lo * b;
+#pragma unroll
+    for (int e = 0; e < D / 4; ++e) o[e] = o[e] * a + __shfl_xor(o[e], w) * b;
+    m = mn;
+  }
+  if (query >= S || grp != 0) return;
 #pragma unroll
   for (int e = 0; e < D / 4; ++e) O[off + (int64_t)query * D + sub * (D / 4) + e] = (float)(o[e] / l);
   if (sub == 0) LSE[blockIdx.y * (int64_t)S + query] = (float)(m + log(l));
@@ -176,7 +198,8 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_f32(const float* __restrict__
 
 hipError_t launch_attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
                                int64_t S, int d, int64_t BH, hipStream_t st) {
-  const dim3 grid((unsigned)((S + kRows - 1) / kRows), (unsigned)BH);
+  constexpr int kQ = 256 / (4 * kSplit);
+  const dim3 grid((unsigned)((S + kQ - 1) / kQ), (unsigned)BH);
   const double scale = 1.0 / sqrt((double)d);
   if (d == 64) attn_fwd_f32<64><<<grid, 256, 0, st>>>(q, k, v, o, lse, (int)S, scale);
   else attn_fwd_f32<128><<<grid, 256, 0, st>>>(q, k, v, o, lse, (int)S, scale);

@@ -62,6 +62,9 @@ struct Plan {
 // for that bound.
 static_assert(LH_POOL_TOKCHUNK <= 64, "token chunks above 64 rows overflow the position cache");
 
+// token-pass row groups below which the chunks shrink: 32 per compute unit
+constexpr int64_t kPoolRowGroupsWanted = 256 * 32;
+
 int lam_max(int p) {
   int lam = 1;
   int64_t pw = p;
@@ -190,9 +193,13 @@ lh_status make_plan(const lh_shape* s, Plan& P) {
       const int lam = std::min(s->L - 1 - lvl, lm);
       int64_t plam = 1;
       for (int i = 0; i < lam; ++i) plam *= s->p;
-      // token passes walk 64-row chunks; upper passes see p^lvl times fewer
-      // rows, so they take one span per row group to keep the GPU busy
-      const int64_t rep = lvl == 0 ? std::max<int64_t>(1, LH_POOL_TOKCHUNK / plam) : 1;
+      // token passes walk 64-row chunks, unless that leaves fewer than
+      // about 32 row groups per compute unit (short sequences, few heads):
+      // then shorter chunks, down to one span of the pass's top level, so
+      // that more row groups share the rows; upper passes see p^lvl times
+      // fewer rows and take one span per row group
+      int64_t rep = lvl == 0 ? std::max<int64_t>(1, LH_POOL_TOKCHUNK / plam) : 1;
+      while (rep > 1 && BH * (s->N / (plam * rep)) < kPoolRowGroupsWanted) rep /= 2;
       const int64_t rows_in = s->N / g.pw[lvl];
       const int64_t brows_in = nvb / g.pw[lvl];
       Stage t{lvl, lam, (int)(plam * rep), rows_in, rows_in / plam, brows_in, brows_in / plam, -1};
@@ -718,7 +725,7 @@ lh_status lh_profile_step(const lh_shape* shape, const void* q, const void* k, c
   for (; made <= LH_PROFILE_STAGES; ++made) {
     const hipError_t e = hipEventCreate(&ev[made]);
     if (e != hipSuccess) {
-      for (int i = 0; i < made; ++i) hipEventDestroy(ev[i]);
+      for (int i = 0; i < made; ++i) (void)hipEventDestroy(ev[i]);
       return hip_fail(e, "hipEventCreate");
     }
   }
@@ -738,7 +745,7 @@ lh_status lh_profile_step(const lh_shape* shape, const void* q, const void* k, c
     const hipEvent_t start = i == 0 ? ev[0] : ev[order[i - 1] + 1];
     e = hipEventElapsedTime(&ms[order[i]], start, ev[order[i] + 1]);
   }
-  for (int i = 0; i <= LH_PROFILE_STAGES; ++i) hipEventDestroy(ev[i]);
+  for (int i = 0; i <= LH_PROFILE_STAGES; ++i) (void)hipEventDestroy(ev[i]);
   if (e != hipSuccess) return hip_fail(e, "profile");
   return s;
 }
