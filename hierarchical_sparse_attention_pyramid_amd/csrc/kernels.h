@@ -13,6 +13,11 @@ namespace lh {
 
 // Maximum pyramid levels one pooling pass produces in registers.
 constexpr int kStageLevels = 3;
+// The token pass's workgroup may form up to kPoolLdsLevels further levels from
+// its rows' top-level float32 sums in LDS (kPoolLdsFloats floats: entries x
+// 3 tensors x d).
+constexpr int kPoolLdsLevels = 3;
+constexpr int kPoolLdsFloats = 6144;
 
 struct PoolFwdArgs {
   const void* in[3];     // stage input: tokens (dtype, layout lin) or f32 sums [BH][in_rows][d]
@@ -25,6 +30,7 @@ struct PoolFwdArgs {
   int32_t lvl0;          // level of the input rows
   int32_t lam;           // levels produced: lvl0+1 .. lvl0+lam
   int32_t chunk;         // input rows per row group (a multiple of p^lam)
+  int32_t xl;            // token pass: further levels lam+1 .. lam+xl formed in LDS
   // the large-head top-K's workspace (hist_stride words per head): every
   // candidate score written (flat index below C) is counted into its pass-0
   // histograms (hist0.h), which must be zero when the first pass starts;
@@ -42,6 +48,7 @@ struct PoolBwdArgs {
   const int32_t* pos;    // [BH][M]
   int64_t in_rows, out_rows;  // virtual rows (see shift)
   int32_t lvl0, lam, chunk;
+  int32_t xl;            // token pass: further levels lam+1 .. lam+xl formed in LDS
   int32_t shift;         // 0: span reading; 1: causal reading (virtual row u = token u - 1)
   Geo g;
 };

@@ -35,6 +35,7 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct Stage {
   int lvl0, lam, chunk;
+  int xl;  // token pass: levels above lvl0 + lam formed in the workgroup through LDS
   int64_t rows_in, rows_out;      // forward pooling: rows per head
   int64_t brows_in, brows_out;    // scatter backward: virtual rows per head
   int out_buf;  // 0 = A, 1 = B, -1 = no f32 sums written
@@ -185,7 +186,7 @@ lh_status make_plan(const lh_shape* s, Plan& P) {
   P.nstages = 0;
   P.sums_rows[0] = P.sums_rows[1] = 0;
   if (s->L == 1) {
-    P.st[P.nstages++] = Stage{0, 0, 64, s->N, s->N, nvb, nvb, -1};
+    P.st[P.nstages++] = Stage{0, 0, 64, 0, s->N, s->N, nvb, nvb, -1};
   } else {
     const int lm = lam_max(s->p);
     int lvl = 0;
@@ -200,11 +201,28 @@ lh_status make_plan(const lh_shape* s, Plan& P) {
       // fewer rows and take one span per row group
       int64_t rep = lvl == 0 ? std::max<int64_t>(1, LH_POOL_TOKCHUNK / plam) : 1;
       while (rep > 1 && BH * (s->N / (plam * rep)) < kPoolRowGroupsWanted) rep /= 2;
+      // The token pass's workgroup covers rgs * chunk consecutive rows; the
+      // levels whose spans divide that (at most kPoolLdsLevels more, p >= 4,
+      // with the top register level's float32 sums of the workgroup in at
+      // most kPoolLdsFloats) are formed from those sums in LDS instead of by
+      // a further pass.
+      int xl = 0;
+      if (lvl == 0 && s->p >= 4) {
+        const int64_t span = (int64_t)(256 / (s->d / 8)) * plam * rep;
+        int64_t pe = plam;
+        if ((span / plam) * 3 * s->d <= lh::kPoolLdsFloats)
+          while (xl < lh::kPoolLdsLevels && lvl + lam + xl < s->L - 1 && span % (pe * s->p) == 0) {
+            pe *= s->p;
+            ++xl;
+          }
+      }
+      int64_t ptop = plam;
+      for (int i = 0; i < xl; ++i) ptop *= s->p;
       const int64_t rows_in = s->N / g.pw[lvl];
       const int64_t brows_in = nvb / g.pw[lvl];
-      Stage t{lvl, lam, (int)(plam * rep), rows_in, rows_in / plam, brows_in, brows_in / plam, -1};
+      Stage t{lvl, lam, (int)(plam * rep), xl, rows_in, rows_in / ptop, brows_in, brows_in / ptop, -1};
       P.st[P.nstages++] = t;
-      lvl += lam;
+      lvl += lam + xl;
     }
     for (int k = 0; k + 1 < P.nstages; ++k) {
       P.st[k].out_buf = k % 2;
@@ -299,6 +317,7 @@ lh_status run_pool(const Plan& P, const void* q, const void* k, const void* v, v
     a.lvl0 = t.lvl0;
     a.lam = t.lam;
     a.chunk = t.chunk;
+    a.xl = t.xl;
     if (do_score && topk_ws != nullptr) {  // count the candidates for the top-K
       a.hist = static_cast<uint32_t*>(topk_ws);
       a.hist_stride = lh::topk_hist_stride(P.g.C);
@@ -569,6 +588,7 @@ static lh_status run_scatter_bwd(const Plan& P, const void* dout, const int32_t*
     a.lvl0 = t.lvl0;
     a.lam = t.lam;
     a.chunk = t.chunk;
+    a.xl = t.xl;
     a.shift = P.sh;
     a.g = P.g;
     LH_HIP(lh::launch_pool_bwd(a, P.dtype, P.BH, s == 0, st), "scatter_backward");

@@ -76,10 +76,14 @@ constexpr int kStageCap = 128;
 // 2 max-pool of stored level-lvl0 scores.  stage (LDS, kStageCap words, or
 // null): the row group's list of candidate score bits written, nst their
 // count; they are counted after the pass, off the row loop.
+// xbuf / xsc (LDS, or null): with a.xl > 0 the top level's float32 sums
+// [entry][tensor][d] and scores of the workgroup's entries (from index xe0
+// of that level) go there instead of to sums_out.
 template <typename Tin, typename Tout, int NT, int SCORE>
 __device__ __forceinline__ void pool_pass(const PoolFwdArgs& a, const int (&tid)[NT],
                                           bool do_pool, int64_t bh, int64_t r0, int nrows,
-                                          int lane, uint32_t* stage, int& nst) {
+                                          int lane, uint32_t* stage, int& nst, float* xbuf,
+                                          float* xsc, int64_t xe0) {
   const Geo& g = a.g;
   const int d = g.d;
   const int lpr = d / 8;
@@ -181,6 +185,17 @@ __device__ __forceinline__ void pool_pass(const PoolFwdArgs& a, const int (&tid)
           }
           if constexpr (SCORE != 0)
             smax[(l + 1) % kStageLevels] = fmaxf(smax[(l + 1) % kStageLevels], smax[l]);
+        } else if (xbuf != nullptr) {
+          const int64_t x = j - xe0;
+          if (do_pool) {
+#pragma unroll
+            for (int i = 0; i < NT; ++i)
+#pragma unroll
+              for (int e = 0; e < 8; ++e) xbuf[(x * 3 + tid[i]) * d + 8 * lane + e] = acc[l][i][e];
+          }
+          if constexpr (SCORE != 0) {
+            if (lane == 0) xsc[x] = smax[l];
+          }
         } else if (do_pool && so[0] != nullptr) {
 #pragma unroll
           for (int i = 0; i < NT; ++i) Row8<float>::store(so[i] + j * d, acc[l][i]);
@@ -195,6 +210,67 @@ __device__ __forceinline__ void pool_pass(const PoolFwdArgs& a, const int (&tid)
   }
 }
 
+// Levels lam+1 .. lam+xl of the token pass from the top register level's
+// float32 sums and scores of the workgroup's E entries (index e0 on), staged
+// in LDS by pool_pass: each new entry sums p consecutive ones in order (the
+// same float32 additions a further pass over the stored sums makes) and
+// takes the max of their scores.  Every thread calls it; at most one sum
+// item (8 elements of one entry's tensor row) and one score per thread and
+// level, which the plan guarantees (p >= 4, E x 3 x d <= kPoolLdsFloats).
+template <typename Tout>
+__device__ __forceinline__ void pool_lds_levels(const PoolFwdArgs& a, int64_t bh, int64_t E,
+                                                int64_t e0, bool do_pool, bool do_score,
+                                                float* xbuf, float* xsc, Hist0Lds* hl,
+                                                uint32_t* hw) {
+  const Geo& g = a.g;
+  const int d = g.d, p = g.p, gpr = d / 8;
+  const int t = threadIdx.x;
+  for (int x = 1; x <= a.xl; ++x) {
+    const int lev = a.lam + x;
+    const int64_t En = E / p, j0 = e0 / p;
+    float s[8];
+    const bool item = do_pool && t < En * 3 * gpr;
+    const int k = t / (3 * gpr), ten = (t / gpr) % 3, g8 = t % gpr;
+    if (item) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s[e] = 0.f;
+      for (int c = 0; c < p; ++c) {
+        const float* src = xbuf + ((k * p + c) * 3 + ten) * d + 8 * g8;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s[e] += src[e];
+      }
+    }
+    const bool sc = do_score && t < En;
+    float sm = neg_inf();
+    if (sc)
+      for (int c = 0; c < p; ++c) sm = fmaxf(sm, xsc[t * p + c]);
+    __syncthreads();  // every read of the level below is done
+    if (item) {
+      const int64_t j = j0 + k;
+      float m[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) m[e] = s[e] * g.inv_pw[lev];
+      Tout* pyr = static_cast<Tout*>(a.pyr[ten]) + bh * (int64_t)(g.M - g.N) * d;
+      Row8<Tout>::template store<kStream>(pyr + (int64_t)(g.base[lev] - g.N + j) * d + 8 * g8, m);
+      if (x < a.xl) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) xbuf[(k * 3 + ten) * d + 8 * g8 + e] = s[e];
+      } else if (a.sums_out[ten] != nullptr) {
+        Row8<float>::store(a.sums_out[ten] + (bh * a.out_rows + j) * d + 8 * g8, s);
+      }
+    }
+    if (sc) {
+      const int64_t flat = g.base[lev] + j0 + t;
+      a.score[bh * g.M + flat] = sm;
+      if (hl != nullptr && flat < g.C) hist0_add(*hl, __float_as_uint(sm), hw);
+      xsc[t] = sm;
+    }
+    __syncthreads();
+    E = En;
+    e0 = j0;
+  }
+}
+
 template <typename Tin, typename Tout, bool FIRST>
 __global__ __launch_bounds__(256) void pool_fwd_kernel(PoolFwdArgs a, int do_pool, int do_score) {
   // the top-K's pass-0 counting (hist0.h) of the candidate scores written:
@@ -203,11 +279,16 @@ __global__ __launch_bounds__(256) void pool_fwd_kernel(PoolFwdArgs a, int do_poo
   __shared__ Hist0Lds hl;
   __shared__ uint32_t stage[32 * kStageCap];
   __shared__ int nstage[32];
+  __shared__ float xbuf[kPoolLdsFloats];
+  __shared__ float xsc[kPoolLdsFloats / 192];
   const bool count = a.hist != nullptr && do_score;  // uniform
+  const bool lds_levels = FIRST && a.xl > 0;         // uniform
   const int lpr = a.g.d / 8;
   const int rgs = 256 / lpr;
   const int rg = threadIdx.x / lpr, lane = threadIdx.x % lpr;
   const int64_t bh = blockIdx.y;
+  const int64_t B0 = (int64_t)blockIdx.x * rgs * a.chunk;  // the workgroup's first row
+  const int64_t xe0 = B0 / a.g.pw[a.lam];                  // its first top-level entry
   int nst = 0;
   if (count) hist0_init(hl);
   const int64_t nchunks = (a.in_rows + a.chunk - 1) / a.chunk;
@@ -216,28 +297,36 @@ __global__ __launch_bounds__(256) void pool_fwd_kernel(PoolFwdArgs a, int do_poo
     const int64_t r0 = c * a.chunk;
     const int nrows = (int)min((int64_t)a.chunk, a.in_rows - r0);
     constexpr int kScore = FIRST ? 1 : 2;
+    float* xb = lds_levels ? xbuf : nullptr;
+    float* xs = lds_levels ? xsc : nullptr;
     // pass 1: q and k (with the scores); pass 2: v (two passes keep fewer
     // rows' accumulators live in registers than one pass over all three)
     const int qk[2] = {0, 1};
     if (do_score) {
       pool_pass<Tin, Tout, 2, kScore>(a, qk, do_pool != 0, bh, r0, nrows, lane,
-                                      count ? stage + rg * kStageCap : nullptr, nst);
+                                      count ? stage + rg * kStageCap : nullptr, nst, xb, xs, xe0);
     } else if (do_pool) {
-      pool_pass<Tin, Tout, 2, 0>(a, qk, true, bh, r0, nrows, lane, nullptr, nst);
+      pool_pass<Tin, Tout, 2, 0>(a, qk, true, bh, r0, nrows, lane, nullptr, nst, xb, xs, xe0);
     }
     if (do_pool) {
       const int vv[1] = {2};
-      pool_pass<Tin, Tout, 1, 0>(a, vv, true, bh, r0, nrows, lane, nullptr, nst);
+      pool_pass<Tin, Tout, 1, 0>(a, vv, true, bh, r0, nrows, lane, nullptr, nst, xb, xs, xe0);
     }
   }
-  if (count) {  // every thread of the workgroup reaches these barriers
-    if (lane == 0) nstage[rg] = nst;
-    __syncthreads();
-    uint32_t* hw = a.hist + bh * a.hist_stride;
+  // every thread of the workgroup reaches the barriers below
+  uint32_t* hw = count ? a.hist + bh * a.hist_stride : nullptr;
+  if (count && lane == 0) nstage[rg] = nst;
+  if (count || lds_levels) __syncthreads();
+  if (count) {
     for (int i = threadIdx.x; i < rgs * kStageCap; i += 256) {
       const int r = i / kStageCap, j = i % kStageCap;
       if (j < nstage[r]) hist0_add(hl, stage[i], hw);
     }
+  }
+  if (lds_levels)
+    pool_lds_levels<Tout>(a, bh, min((int64_t)rgs * a.chunk, a.in_rows - B0) / a.g.pw[a.lam], xe0,
+                          do_pool != 0, do_score != 0, xbuf, xsc, count ? &hl : nullptr, hw);
+  if (count) {
     __syncthreads();
     hist0_flush(hl, hw);
   }
@@ -257,7 +346,7 @@ __global__ __launch_bounds__(256) void pool_fwd_kernel(PoolFwdArgs a, int do_poo
 constexpr int kBwdPosCache = 4608;  // ints: workgroup rows + their ancestors (p >= 2)
 
 template <typename Tin, typename Tout, bool FIRST, int SH>
-__global__ __launch_bounds__(256) void pool_bwd_kernel(PoolBwdArgs a) {
+__global__ __launch_bounds__(256, (FIRST && sizeof(Tin) == 2) ? 5 : 1) void pool_bwd_kernel(PoolBwdArgs a) {
   const Geo& g = a.g;
   const int d = g.d;
   const int lpr = d / 8;
@@ -301,9 +390,13 @@ __global__ __launch_bounds__(256) void pool_bwd_kernel(PoolBwdArgs a) {
     off += jhi - jlo + 1;
   }
   __syncthreads();
-  if (c >= nchunks) return;  // no barrier below
   auto posf = [&](int l, int32_t j) { return sp[soff[l] + (j - sjlo[l])]; };
-
+  // token pass with a.xl > 0: the top register level's float32 sums of the
+  // workgroup's entries (from xe0) are staged in LDS for the levels above
+  __shared__ float xbuf[kPoolLdsFloats / 3];
+  const bool lds_levels = FIRST && a.xl > 0;  // uniform
+  const int64_t xe0 = B0 / g.pw[a.lam];
+  if (c < nchunks) {
   const int64_t r0 = c * a.chunk;
   const int nrows = (int)min((int64_t)a.chunk, a.in_rows - r0);
   const Tin* in = static_cast<const Tin*>(a.in) + a.lin.head(bh) + 8 * lane;
@@ -387,6 +480,9 @@ __global__ __launch_bounds__(256) void pool_bwd_kernel(PoolBwdArgs a) {
         if (l + 1 < kStageLevels && l + 1 < a.lam) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) acc[(l + 1) % kStageLevels][e] += acc[l][e];
+        } else if (lds_levels) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) xbuf[(j - xe0) * d + 8 * lane + e] = acc[l][e];
         } else if (so != nullptr) {
           Row8<float>::store(so + j * d, acc[l]);
         }
@@ -394,6 +490,47 @@ __global__ __launch_bounds__(256) void pool_bwd_kernel(PoolBwdArgs a) {
         for (int e = 0; e < 8; ++e) acc[l][e] = 0.f;
       }
     }
+  }
+  }  // c < nchunks
+  if (!lds_levels) return;
+  // levels lam+1 .. lam+xl: each entry sums p consecutive staged ones in order
+  // (the float32 additions a further pass over stored sums makes); selected
+  // entries are written to dos; the top one's sums go to sums_out.  At most
+  // one 8-element item per thread and level (the plan guarantees it).
+  __syncthreads();  // every staged sum is in LDS
+  const int gpr = d / 8, t = threadIdx.x;
+  int64_t E = BT / g.pw[a.lam], e0 = xe0;
+  for (int x = 1; x <= a.xl; ++x) {
+    const int lev = a.lam + x;
+    const int64_t En = E / g.p, j0 = e0 / g.p;
+    const bool item = t < En * gpr;
+    const int k = t / gpr, g8 = t % gpr;
+    float sx[8];
+    if (item) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sx[e] = 0.f;
+      for (int cc = 0; cc < g.p; ++cc) {
+        const float* src = xbuf + (k * g.p + cc) * d + 8 * g8;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sx[e] += src[e];
+      }
+    }
+    __syncthreads();  // every read of the level below is done
+    if (item) {
+      const int64_t j = j0 + k;
+      const int32_t pe = posf(lev, (int32_t)j);
+      if (pe >= 0)
+        Row8<Tout>::store(static_cast<Tout*>(a.dos) + (bh * (int64_t)g.S + pe) * d + 8 * g8, sx);
+      if (x < a.xl) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) xbuf[k * d + 8 * g8 + e] = sx[e];
+      } else if (a.sums_out != nullptr) {
+        Row8<float>::store(a.sums_out + (bh * a.out_rows + j) * d + 8 * g8, sx);
+      }
+    }
+    __syncthreads();
+    E = En;
+    e0 = j0;
   }
 }
 

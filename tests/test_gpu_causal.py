@@ -35,6 +35,7 @@ CASES = [
     ("c_p2_deep_bf16", 1, 2, 4096, 128, 2, 12, 700, "bf16"),   # several pooling passes
     ("c_p64_bf16", 1, 2, 8192, 64, 64, 3, 400, "bf16"),
     ("c_dense_bf16", 1, 1, 300, 128, 4, 1, 300, "bf16"),        # L = 1
+    ("c_lds_p4_L6_d128_bf16", 1, 1, 9216, 128, 4, 6, 700, "bf16"),  # two levels formed in LDS
 ]
 ids = [c[0] for c in CASES]
 _cache: dict = {}

@@ -43,6 +43,13 @@ CASES = [
     # above 16384 candidates per head the pooling kernel counts the top-K's
     # first histogram pass; repeated rows tie scores across its slices
     ("ties_n32k_bf16", 1, 2, 32768, 64, 4, 3, 3000, "bf16"),
+    # levels above the token pass's registers formed through LDS in its
+    # workgroup: one level with a partial last workgroup, two levels, two
+    # levels and a further pass, p = 8
+    ("lds_p4_L5_ragged_bf16", 1, 2, 4352, 64, 4, 5, 500, "bf16"),
+    ("lds_p4_L6_d128_fp32", 1, 1, 9216, 128, 4, 6, 700, "fp32"),
+    ("lds_p4_L7_d128_bf16", 1, 1, 16384, 128, 4, 7, 900, "bf16"),
+    ("lds_p8_L4_bf16", 1, 2, 4096, 64, 8, 4, 300, "bf16"),
 ]
 ids = [c[0] for c in CASES]
 _cache: dict = {}
