@@ -156,3 +156,17 @@ def test_subsequence_byte_size_limit(lb, N, d, ok):
         with pytest.raises(lb.LighthouseError) as ei:
             lb.lh_query_sizes(shape)
         assert ei.value.status == 2
+
+
+@pytest.mark.parametrize("B,H,N,d,p,L,S,one_pass", [
+    (1, 16, 98304, 64, 4, 5, 8192, True),      # levels 1-3 in registers, 4 through LDS
+    (1, 16, 524288, 128, 4, 6, 16384, True),   # levels 4 and 5 through LDS
+    (1, 16, 1048576, 128, 4, 7, 32768, False),  # level 6 needs a further pass
+    (1, 2, 4096, 128, 2, 12, 700, False),      # p = 2: register levels only
+])
+def test_pooling_passes_from_the_plan(lb, B, H, N, d, p, L, S, one_pass):
+    """The token pass forms the levels whose spans divide its workgroup's rows
+    through LDS; only deeper pyramids need float32 sums for a further pass
+    (workspace ws_build_pyramid)."""
+    z = lb.lh_query_sizes(lb.make_shape(B, H, N, d, p, L, S, 1))  # bf16
+    assert (z.ws_build_pyramid == 0) == one_pass
