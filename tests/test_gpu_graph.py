@@ -16,7 +16,8 @@ from tests.test_gpu_parity import CASES, run_case
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("name", ["d128_ragged_bf16", "p2_deep_b2_fp32", "ties_bf16", "only_coarse_fp32"])
+@pytest.mark.parametrize("name", ["d128_ragged_bf16", "p2_deep_b2_fp32", "ties_bf16", "only_coarse_fp32",
+                                  "ties_n32k_bf16", "lds_p4_L6_d128_fp32"])
 def test_graph_replays_match_eager(name, gpu_lib):
     lb = gpu_lib
     case = next(c for c in CASES if c[0] == name)
