@@ -10,10 +10,11 @@
 // Mapping: a row of d elements is covered by d/8 lanes (8 elements each, one
 // 16-byte bf16 or 32-byte fp32 access); a 256-thread block holds 256/(d/8)
 // such row groups.  Each row group walks one chunk of consecutive input rows
-// in order and keeps one running float32 sum per level in registers, so each
-// input row is read exactly once and every level is produced in the same
-// pass.  Deep pyramids use several passes: a pass hands the float32 sums of
-// its top level to the next one.
+// in order and keeps one running float32 sum per level in registers (up to
+// three levels), so each input row is read exactly once.  On the token pass
+// the workgroup then forms the levels whose spans divide its rows from the
+// row groups' top-level sums in LDS (p >= 4).  Deeper pyramids use further
+// passes: a pass hands the float32 sums of its top level to the next one.
 #include "hist0.h"
 #include "kernels.h"
 #include "walk.h"
