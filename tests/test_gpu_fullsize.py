@@ -46,9 +46,10 @@ def to_dev(a, dtype):
 
 
 # the causal scatter reading at full size: the headline workload (fast
-# scatter kernels), the small fp32 workload and the p = 2 operating point
-# (generic ancestor-walk kernels)
-CAUSAL = ["train_n98k_bf16", "fwd_n4k_fp32", "op_n98k_p2_bf16"]
+# scatter kernels), the 512K workload (two pyramid levels formed in LDS over
+# the padded virtual rows), the small fp32 workload and the p = 2 operating
+# point (generic ancestor-walk kernels)
+CAUSAL = ["train_n98k_bf16", "long_n512k_bf16", "fwd_n4k_fp32", "op_n98k_p2_bf16"]
 CASES = [(n, "span") for n in WORKLOADS] + [(n, "causal") for n in CAUSAL]
 
 
