@@ -141,3 +141,28 @@ def test_stage_entry_points_on_strided_tokens(name, gpu_lib):
         torch.cuda.synchronize()
         for i, (x, y) in enumerate(zip(a, b_)):
             assert torch.equal(x, y), f"{stage.__name__}[{i}]: strided differs from packed"
+
+
+@pytest.mark.parametrize("name", ["d128_ragged_bf16", "p3_bf16", "lds_p4_L5_ragged_bf16"])
+def test_causal_reading_on_strided_tokens(name, gpu_lib):
+    """The causal scatter reading on strided token tensors equals its packed
+    run bit for bit (the packed causal runs are compared with the oracle in
+    test_gpu_causal.py)."""
+    lb = gpu_lib
+    case = next(c for c in CASES if c[0] == name)
+    R = run_case(case)
+    _, B, H, N, d, p, L, S, dt = case
+    print(f"[strided] causal {name}", flush=True)
+    host = {t: to_device(R["host"][t], dt) for t in ("q", "k", "v", "dout")}
+    ref_out, ref_bufs, ref_shape = lb.forward(host["q"], host["k"], host["v"], p, L, S,
+                                              scatter="causal")
+    ref = (ref_out, *lb.backward(ref_shape, host["dout"], ref_bufs))
+    _, (q, k, v) = packed_tokens([host["q"], host["k"], host["v"]])
+    _, (dout,) = packed_tokens([host["dout"]])
+    o_buf, (out,) = packed_tokens([torch.empty_like(host["q"])])
+    g_buf, (dq, dk, dv) = packed_tokens([torch.empty_like(host["q"]) for _ in range(3)])
+    out, bufs, shape = lb.forward(q, k, v, p, L, S, out=out, scatter="causal")
+    lb.backward(shape, dout, bufs, dq, dk, dv)
+    torch.cuda.synchronize()
+    for key, got, want in zip(("out", "dq", "dk", "dv"), (out, dq, dk, dv), ref):
+        assert torch.equal(got, want), f"{key}: strided causal run differs from the packed run"
