@@ -579,9 +579,27 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void attn_bwd_dkdv_bf16(
   // register file would otherwise spill); they are the B operand of dP.
   constexpr bool kVInLds = D == 128 && LH_BKV128_VLDS;
   constexpr bool kEach = D == 128;  // register budget: one XOR per LDS read
-  __shared__ __attribute__((aligned(1024))) __bf16 sT[2][2][C::kTile];  // [buffer][Q, dO]
+  // Q, dO, lse and rowsum tiles in two buffers each.  d = 64: every buffer
+  // its own array and each tile step compiled for one parity, so that the
+  // step's LDS reads need not wait for the next tile's direct loads (2-3%
+  // faster).  d = 128: one array of all four tiles and one loop body, the
+  // parity a run-time offset of the lane part of each read: there the
+  // register file is full, and both the parity copies and a shared helper
+  // for the slice code (as d = 64 uses) raise the spills from 23 to 39 or
+  // more, which costs 10%, so that path keeps its own copy of the slices.
+  constexpr bool kSplit = D == 64;
+  constexpr int kT1 = kSplit ? C::kTile : 8, kQ1 = kSplit ? C::kQT : 1;
+  __shared__ __attribute__((aligned(1024))) __bf16 sQ0[kSplit ? C::kTile : 4 * C::kTile];
+  __shared__ __attribute__((aligned(1024))) __bf16 sG0[kT1];
+  __shared__ __attribute__((aligned(1024))) __bf16 sQ1[kT1];
+  __shared__ __attribute__((aligned(1024))) __bf16 sG1[kT1];
   __shared__ __attribute__((aligned(1024))) __bf16 sVw[kVInLds ? WAVES : 1][kVInLds ? 32 * D : 8];
-  __shared__ float sLD[2][2][C::kQT];                                  // [buffer][lse, delta]
+  __shared__ float sL0[kSplit ? C::kQT : 4 * C::kQT], sD0[kQ1], sL1[kQ1], sD1[kQ1];
+  // tiles of parity P: Q, dO, lse, rowsum
+  auto tQ = [&](int P) __attribute__((always_inline)) { return kSplit ? (P ? sQ1 : sQ0) : sQ0 + 2 * P * C::kTile; };
+  auto tG = [&](int P) __attribute__((always_inline)) { return kSplit ? (P ? sG1 : sG0) : sQ0 + (2 * P + 1) * C::kTile; };
+  auto tL = [&](int P) __attribute__((always_inline)) { return kSplit ? (P ? sL1 : sL0) : sL0 + 2 * P * C::kQT; };
+  auto tD = [&](int P) __attribute__((always_inline)) { return kSplit ? (P ? sD1 : sD0) : sL0 + (2 * P + 1) * C::kQT; };
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
   const int h = lane >> 5, c32 = lane & 31;
@@ -602,13 +620,13 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void attn_bwd_dkdv_bf16(
 
   const int t0 = kb0 / C::kQT;
   const int ntiles = (S + C::kQT - 1) / C::kQT;
-  auto issue = [&](int t, int buf) {
-    load_tile<D, C::kQT, WAVES>(Q + off, S, t * C::kQT, sT[buf][0], wave, lane);
-    load_tile<D, C::kQT, WAVES>(dO + off, S, t * C::kQT, sT[buf][1], wave, lane);
-    if (wave == 0) load_vec64(lse_h, S, t * C::kQT, sLD[buf][0], lane);
-    if (wave == WAVES - 1) load_vec64(del_h, S, t * C::kQT, sLD[buf][1], lane);
+  auto issue = [&](int P, int t) __attribute__((always_inline)) {
+    load_tile<D, C::kQT, WAVES>(Q + off, S, t * C::kQT, tQ(P), wave, lane);
+    load_tile<D, C::kQT, WAVES>(dO + off, S, t * C::kQT, tG(P), wave, lane);
+    if (wave == 0) load_vec64(lse_h, S, t * C::kQT, tL(P), lane);
+    if (wave == WAVES - 1) load_vec64(del_h, S, t * C::kQT, tD(P), lane);
   };
-  issue(t0, 0);
+  issue(0, t0);
 
   bf16x8 kreg[D / 16], vreg[kVInLds ? 1 : D / 16];
 #pragma unroll
@@ -628,19 +646,20 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void attn_bwd_dkdv_bf16(
     dva[mb] = zero16();
   }
 
-  for (int t = t0; t < ntiles; ++t) {
-    const int buf = (t - t0) & 1;
+  // d = 64: query tile t in the buffers of parity PAR = (t - t0) & 1
+  auto tile_step = [&](auto par, int t) __attribute__((always_inline)) {
+    constexpr int PAR = decltype(par)::value;
+    const __bf16* bQ = tQ(PAR);
+    const __bf16* bG = tG(PAR);
+    const float* sL = tL(PAR);
+    const float* sD = tD(PAR);
     const int q0 = t * C::kQT;
     wait_loads();
     __syncthreads();
-    if (t + 1 < ntiles) issue(t + 1, buf ^ 1);
-    if (kw0 >= S || q0 + C::kQT - 1 < kw0) continue;
-    const uint32_t tbo = (uint32_t)(buf * 2 * C::kTile * 2);  // Q tile; the dO tile follows
+    if (t + 1 < ntiles) issue(1 - PAR, t + 1);
+    if (kw0 >= S || q0 + C::kQT - 1 < kw0) return;
     const uint32_t lvt = lvw;
-    const uint32_t lq = lrow ^ tbo, lg = lrow ^ (tbo + C::kTile * 2);
-    const uint32_t tq = ltr ^ tbo, tg = ltr ^ (tbo + C::kTile * 2);
-    const float* sL = sLD[buf][0];
-    const float* sD = sLD[buf][1];
+    const uint32_t lq = lrow, lg = lrow, tq = ltr, tg = ltr;
 #pragma unroll
     for (int qs = 0; qs < 2; ++qs) {
       // d = 128: keep the scheduler from hoisting the next slice's reads
@@ -651,9 +670,9 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void attn_bwd_dkdv_bf16(
       f32x16 sacc = zero16(), dpacc = zero16();
 #pragma unroll
       for (int dc = 0; dc < D / 16; ++dc) {
-        sacc = mfma32(lds_rows<D, kEach>(sT, lq, qs * 32, dc), kreg[dc], sacc);
+        sacc = mfma32(lds_rows<D, kEach>(bQ, lq, qs * 32, dc), kreg[dc], sacc);
         const bf16x8 vb = kVInLds ? lds_rows<D, kEach>(sVw, lvt, 0, dc) : vreg[kVInLds ? 0 : dc];
-        dpacc = mfma32(lds_rows<D, kEach>(sT, lg, qs * 32, dc), vb, dpacc);
+        dpacc = mfma32(lds_rows<D, kEach>(bG, lg, qs * 32, dc), vb, dpacc);
       }
       // Only a slice that meets the diagonal or the end of the sequence needs
       // masks (a wave-uniform branch keeps them off every other slice).
@@ -666,9 +685,59 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void attn_bwd_dkdv_bf16(
       for (int c = 0; c < 2; ++c)
 #pragma unroll
         for (int mb = 0; mb < D / 32; ++mb) {
-          dva[mb] = mfma32(lds_tr8<D, kEach>(sT, tg, qs * 32 + 16 * c, mb * 32), pch[c], dva[mb]);
-          dka[mb] = mfma32(lds_tr8<D, kEach>(sT, tq, qs * 32 + 16 * c, mb * 32), dsch[c], dka[mb]);
+          dva[mb] = mfma32(lds_tr8<D, kEach>(bG, tg, qs * 32 + 16 * c, mb * 32), pch[c], dva[mb]);
+          dka[mb] = mfma32(lds_tr8<D, kEach>(bQ, tq, qs * 32 + 16 * c, mb * 32), dsch[c], dka[mb]);
         }
+    }
+  };
+  if constexpr (kSplit) {
+    for (int t = t0; t < ntiles; t += 2) {
+      tile_step(std::integral_constant<int, 0>{}, t);
+      if (t + 1 < ntiles) tile_step(std::integral_constant<int, 1>{}, t + 1);
+    }
+  } else {  // d = 128
+    for (int t = t0; t < ntiles; ++t) {
+      const int buf = (t - t0) & 1;
+      const int q0 = t * C::kQT;
+      wait_loads();
+      __syncthreads();
+      if (t + 1 < ntiles) issue(buf ^ 1, t + 1);
+      if (kw0 >= S || q0 + C::kQT - 1 < kw0) continue;
+      const uint32_t tbo = (uint32_t)(buf * 2 * C::kTile * 2);  // Q tile; the dO tile follows
+      const uint32_t lvt = lvw;
+      const uint32_t lq = lrow ^ tbo, lg = lrow ^ (tbo + C::kTile * 2);
+      const uint32_t tq = ltr ^ tbo, tg = ltr ^ (tbo + C::kTile * 2);
+      const float* sL = tL(buf);
+      const float* sD = tD(buf);
+#pragma unroll
+      for (int qs = 0; qs < 2; ++qs) {
+        // d = 128: keep the scheduler from hoisting the next slice's reads
+        // (their registers would push live values out to scratch)
+        if constexpr (kEach) __builtin_amdgcn_sched_barrier(0);
+        const int qbase = q0 + qs * 32;
+        if (qbase + 31 < kw0) continue;
+        f32x16 sacc = zero16(), dpacc = zero16();
+#pragma unroll
+        for (int dc = 0; dc < D / 16; ++dc) {
+          sacc = mfma32(lds_rows<D, kEach>(sQ0, lq, qs * 32, dc), kreg[dc], sacc);
+          const bf16x8 vb = kVInLds ? lds_rows<D, kEach>(sVw, lvt, 0, dc) : vreg[kVInLds ? 0 : dc];
+          dpacc = mfma32(lds_rows<D, kEach>(sQ0, lg, qs * 32, dc), vb, dpacc);
+        }
+        // Only a slice that meets the diagonal or the end of the sequence needs
+        // masks (a wave-uniform branch keeps them off every other slice).
+        bf16x8 pch[2], dsch[2];
+        if (qbase < kw0 + 31 || q0 + C::kQT > S)
+          kv_weights<true>(sacc, dpacc, sL, sD, qs, h, sl2, key, q0, S, pch, dsch);
+        else
+          kv_weights<false>(sacc, dpacc, sL, sD, qs, h, sl2, key, q0, S, pch, dsch);
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+          for (int mb = 0; mb < D / 32; ++mb) {
+            dva[mb] = mfma32(lds_tr8<D, kEach>(sQ0, tg, qs * 32 + 16 * c, mb * 32), pch[c], dva[mb]);
+            dka[mb] = mfma32(lds_tr8<D, kEach>(sQ0, tq, qs * 32 + 16 * c, mb * 32), dsch[c], dka[mb]);
+          }
+      }
     }
   }
   if (key < S) {
@@ -727,7 +796,19 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void attn_bwd_dq_bf16(
     float* __restrict__ LSE2, float* __restrict__ DELTA, float* __restrict__ dQ, int S, float sl2,
     float scale, int paired) {
   using C = BwdQCfg<D, WAVES>;
-  __shared__ __attribute__((aligned(1024))) __bf16 sKV[2][2][C::kTile];  // [buffer][K, V]
+  // K and V tiles in two buffers each.  d = 64: every buffer its own array
+  // and each tile step compiled for one parity (reads need not wait for the
+  // loads); d = 128: one array and one loop body, the parity a run-time offset
+  // of the lane part of each read (the register budget of the key-block
+  // pass, kept alike here)
+  constexpr bool kSplit = D == 64;
+  constexpr int kT1 = kSplit ? C::kTile : 8;
+  __shared__ __attribute__((aligned(1024))) __bf16 sK0[kSplit ? C::kTile : 4 * C::kTile];
+  __shared__ __attribute__((aligned(1024))) __bf16 sV0[kT1];
+  __shared__ __attribute__((aligned(1024))) __bf16 sK1[kT1];
+  __shared__ __attribute__((aligned(1024))) __bf16 sV1[kT1];
+  auto tK = [&](int P) __attribute__((always_inline)) { return kSplit ? (P ? sK1 : sK0) : sK0 + 2 * P * C::kTile; };
+  auto tV = [&](int P) __attribute__((always_inline)) { return kSplit ? (P ? sV1 : sV0) : sK0 + (2 * P + 1) * C::kTile; };
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
   const int h = lane >> 5, c32 = lane & 31;
@@ -745,8 +826,8 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void attn_bwd_dq_bf16(
 
   const int kend = min(S, q0 + C::kQB);
   const int ntiles = (kend + C::kKT - 1) / C::kKT;
-  load_tile<D, C::kKT, WAVES>(K + off, S, 0, sKV[0][0], wave, lane);
-  load_tile<D, C::kKT, WAVES>(V + off, S, 0, sKV[0][1], wave, lane);
+  load_tile<D, C::kKT, WAVES>(K + off, S, 0, tK(0), wave, lane);
+  load_tile<D, C::kKT, WAVES>(V + off, S, 0, tV(0), wave, lane);
 
   bf16x8 qreg[D / 16], doreg[D / 16];
 #pragma unroll
@@ -786,17 +867,21 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void attn_bwd_dq_bf16(
 #pragma unroll
   for (int i = 0; i < 16; ++i) negdl[i] = -dl;
 
-  for (int kt = 0; kt < ntiles; ++kt) {
+  // key tile kt, held in the buffers of parity kt & 1 = PAR
+  // d = 64: key tile kt in the buffers of parity PAR = kt & 1
+  auto tile_step = [&](auto par, int kt) __attribute__((always_inline)) {
+    constexpr int PAR = decltype(par)::value;
+    const __bf16* bK = tK(PAR);
+    const __bf16* bV = tV(PAR);
     const int k0 = kt * C::kKT;
     wait_loads();
     __syncthreads();
     if (kt + 1 < ntiles) {
-      load_tile<D, C::kKT, WAVES>(K + off, S, k0 + C::kKT, sKV[(kt + 1) & 1][0], wave, lane);
-      load_tile<D, C::kKT, WAVES>(V + off, S, k0 + C::kKT, sKV[(kt + 1) & 1][1], wave, lane);
+      load_tile<D, C::kKT, WAVES>(K + off, S, k0 + C::kKT, tK(1 - PAR), wave, lane);
+      load_tile<D, C::kKT, WAVES>(V + off, S, k0 + C::kKT, tV(1 - PAR), wave, lane);
     }
-    if (qw0 >= S || k0 > qw0 + C::kQW - 1) continue;
-    const uint32_t kbo = (uint32_t)((kt & 1) * 2 * C::kTile * 2);  // K tile; the V tile follows
-    const uint32_t lk = lrow ^ kbo, lv = lrow ^ (kbo + C::kTile * 2), tk = ltr ^ kbo;
+    if (qw0 >= S || k0 > qw0 + C::kQW - 1) return;
+    const uint32_t lk = lrow, lv = lrow, tk = ltr;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const int kbase = k0 + kb * 32;
@@ -804,8 +889,8 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void attn_bwd_dq_bf16(
       f32x16 sacc = zero16(), dpacc = negdl;
 #pragma unroll
       for (int dc = 0; dc < D / 16; ++dc) {
-        sacc = mfma32(lds_rows<D>(sKV, lk, kb * 32, dc), qreg[dc], sacc);
-        dpacc = mfma32(lds_rows<D>(sKV, lv, kb * 32, dc), doreg[dc], dpacc);
+        sacc = mfma32(lds_rows<D>(bK, lk, kb * 32, dc), qreg[dc], sacc);
+        dpacc = mfma32(lds_rows<D>(bV, lv, kb * 32, dc), doreg[dc], dpacc);
       }
       bf16x8 dsch[2];
       if (kbase + 31 > qw0)  // diagonal slice (wave-uniform)
@@ -816,7 +901,47 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void attn_bwd_dq_bf16(
       for (int c = 0; c < 2; ++c)
 #pragma unroll
         for (int mb = 0; mb < D / 32; ++mb)
-          dqa[mb] = mfma32(lds_tr8<D>(sKV, tk, kb * 32 + 16 * c, mb * 32), dsch[c], dqa[mb]);
+          dqa[mb] = mfma32(lds_tr8<D>(bK, tk, kb * 32 + 16 * c, mb * 32), dsch[c], dqa[mb]);
+    }
+  };
+  if constexpr (kSplit) {
+    for (int kt = 0; kt < ntiles; kt += 2) {
+      tile_step(std::integral_constant<int, 0>{}, kt);
+      if (kt + 1 < ntiles) tile_step(std::integral_constant<int, 1>{}, kt + 1);
+    }
+  } else {  // d = 128
+    for (int kt = 0; kt < ntiles; ++kt) {
+      const int k0 = kt * C::kKT;
+      wait_loads();
+      __syncthreads();
+      if (kt + 1 < ntiles) {
+        load_tile<D, C::kKT, WAVES>(K + off, S, k0 + C::kKT, sK0 + 2 * ((kt + 1) & 1) * C::kTile, wave, lane);
+        load_tile<D, C::kKT, WAVES>(V + off, S, k0 + C::kKT, sK0 + (2 * ((kt + 1) & 1) + 1) * C::kTile, wave, lane);
+      }
+      if (qw0 >= S || k0 > qw0 + C::kQW - 1) continue;
+      const uint32_t kbo = (uint32_t)((kt & 1) * 2 * C::kTile * 2);  // K tile; the V tile follows
+      const uint32_t lk = lrow ^ kbo, lv = lrow ^ (kbo + C::kTile * 2), tk = ltr ^ kbo;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const int kbase = k0 + kb * 32;
+        if (kbase > qw0 + 31) continue;
+        f32x16 sacc = zero16(), dpacc = negdl;
+#pragma unroll
+        for (int dc = 0; dc < D / 16; ++dc) {
+          sacc = mfma32(lds_rows<D>(sK0, lk, kb * 32, dc), qreg[dc], sacc);
+          dpacc = mfma32(lds_rows<D>(sK0, lv, kb * 32, dc), doreg[dc], dpacc);
+        }
+        bf16x8 dsch[2];
+        if (kbase + 31 > qw0)  // diagonal slice (wave-uniform)
+          q_weights<true>(sacc, dpacc, lse2, sl2, kbase, h, query, dsch);
+        else
+          q_weights<false>(sacc, dpacc, lse2, sl2, kbase, h, query, dsch);
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+          for (int mb = 0; mb < D / 32; ++mb)
+            dqa[mb] = mfma32(lds_tr8<D>(sK0, tk, kb * 32 + 16 * c, mb * 32), dsch[c], dqa[mb]);
+      }
     }
   }
   if (query < S) {
