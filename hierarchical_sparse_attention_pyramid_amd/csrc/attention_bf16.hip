@@ -999,8 +999,8 @@ hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, float* o
 hipError_t launch_attn_bwd(const void* q, const void* k, const void* v, const float* o,
                            const float* lse, const void* dout, float* dq, float* dk, float* dv,
                            float* delta, float* lse2, int64_t S, int d, int dtype, int64_t BH,
-                           hipStream_t st, hipEvent_t* ev) {
-  if (S == 0) return hipSuccess;
+                           hipStream_t st, hipEvent_t* ev, hipEvent_t dq_done) {
+  if (S == 0) return dq_done ? hipEventRecord(dq_done, st) : hipSuccess;
   const int64_t rows = S * BH;
   const int rgs = 256 / (d / 8);
   const unsigned dgrid = (unsigned)((rows + rgs - 1) / rgs);
@@ -1018,6 +1018,7 @@ hipError_t launch_attn_bwd(const void* q, const void* k, const void* v, const fl
     e = launch_attn_bwd_f32(static_cast<const float*>(q), static_cast<const float*>(k),
                             static_cast<const float*>(v), lse, delta,
                             static_cast<const float*>(dout), dq, dk, dv, S, d, BH, st, ev);
+    if (e == hipSuccess && dq_done) e = hipEventRecord(dq_done, st);  // dQ is the last pass
     return e;
   }
   const float scale = 1.0f / sqrtf((float)d);
@@ -1043,6 +1044,7 @@ hipError_t launch_attn_bwd(const void* q, const void* k, const void* v, const fl
   }
   e = hipGetLastError();
   if (e == hipSuccess && ev) e = hipEventRecord(ev[2], st);
+  if (e == hipSuccess && dq_done) e = hipEventRecord(dq_done, st);
   if (e != hipSuccess) return e;
   if (d == 64) {
     auto dkdv64 = [&](auto waves) {

@@ -95,6 +95,7 @@ hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, float* o
 hipError_t launch_attn_bwd(const void* q, const void* k, const void* v, const float* o,
                            const float* lse, const void* dout, float* dq, float* dk, float* dv,
                            float* delta, float* lse2, int64_t S, int d, int dtype, int64_t BH,
-                           hipStream_t st, hipEvent_t* ev);  // ev: ends of rowsum, dK/dV, dQ
+                           hipStream_t st, hipEvent_t* ev,  // ev: ends of rowsum, dK/dV, dQ
+                           hipEvent_t dq_done = nullptr);   // bf16: recorded after the dQ pass
 
 }  // namespace lh

@@ -679,9 +679,71 @@ static lh_status check_backward_args(const void* dout, const lh_buffers* b, void
   return LH_OK;
 }
 
+#ifndef LH_BWD_FORK
+#define LH_BWD_FORK 1
+#endif
+
+// The side stream of lh_backward on one device, with the events of its fork
+// and join: one set per host thread and device, made on first use and kept
+// until the process ends (so no two threads share one, and a thread's calls
+// are ordered on it as on their own streams).
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+
+// The calling thread's side stream for the device of `st`, or null when the
+// backward should run on `st` alone: `st` belongs to another device than the
+// current one; the side stream does not exist yet and `st` is being captured
+// into a graph (it is made only outside captures, where making it cannot
+// disturb one: a capture thus forks only after an eager call on the thread);
+// the side stream is part of a graph capture that `st` is not (one still
+// open from an earlier call); or a HIP call fails (the sequential path then
+// reports any real error itself).
+static SideStream* side_stream(hipStream_t st) {
+  constexpr int kMaxDevices = 64;
+  thread_local SideStream side[kMaxDevices];
+  int dev = -1, sdev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  if (hipStreamGetDevice(st, &sdev) != hipSuccess || sdev != dev) return nullptr;
+  hipStreamCaptureStatus cm = hipStreamCaptureStatusNone;
+  unsigned long long im = 0;
+  if (hipStreamGetCaptureInfo(st, &cm, &im) != hipSuccess) return nullptr;
+  SideStream& sd = side[dev];
+  if (!sd.s) {
+    if (cm != hipStreamCaptureStatusNone) return nullptr;
+    hipStream_t s = nullptr;
+    hipEvent_t f = nullptr, j = nullptr;
+    if (hipStreamCreateWithFlags(&s, hipStreamNonBlocking) != hipSuccess) return nullptr;
+    if (hipEventCreateWithFlags(&f, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&j, hipEventDisableTiming) != hipSuccess) {
+      if (f) (void)hipEventDestroy(f);
+      (void)hipStreamDestroy(s);
+      return nullptr;
+    }
+    sd.s = s;
+    sd.fork = f;
+    sd.join = j;
+  }
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  unsigned long long is = 0;
+  if (hipStreamGetCaptureInfo(sd.s, &cs, &is) != hipSuccess) return nullptr;
+  if (cs != hipStreamCaptureStatusNone && (cm != hipStreamCaptureStatusActive || im != is))
+    return nullptr;
+  if (cm != hipStreamCaptureStatusNone && cm != hipStreamCaptureStatusActive) return nullptr;
+  return &sd;
+}
+
 // Backward launch sequence; when `ev` is given, ev[i] is recorded after stage
 // i (scatter backward, delta, dK/dV pass, dQ pass, gather backward), in the
 // order the stages run (bf16: the dQ pass, which forms delta, before dK/dV).
+// Without `ev`, with bf16 storage and d = 64, the gather backward of dq runs
+// on a side stream beside the dK/dV pass (it needs only the dQ pass, which
+// runs first): the broadcast is bound by HBM and the key-block pass by the
+// matrix cores, and at d = 64 a compute unit has room for both, so they
+// overlap (the 98K step 1% faster); `st` waits for the side stream at the
+// end.  At d = 128 the key-block pass fills the compute units' registers,
+// the broadcast could only follow it, and the fork measured 0.7% slower.
 static lh_status run_backward(const Plan& P, const void* dout, const lh_buffers* b, void* dq,
                               void* dk, void* dv, void* ws, hipStream_t st, hipEvent_t* ev) {
   char* w = static_cast<char*>(ws);
@@ -699,8 +761,11 @@ static lh_status run_backward(const Plan& P, const void* dout, const lh_buffers*
   lh_status s;
   if ((s = run_scatter_bwd(P, dout, b->pos, dos, w, st)) != LH_OK) return s;
   if (ev) LH_HIP(hipEventRecord(ev[0], st), "event");
+  SideStream* side =
+      LH_BWD_FORK && !ev && P.dtype == 1 && P.g.d == 64 && P.g.S > 0 ? side_stream(st) : nullptr;
   LH_HIP(lh::launch_attn_bwd(b->qs, b->ks, b->vs, b->os, b->lse, dos, dqs, dks, dvs, delta, lse2,
-                             P.g.S, P.g.d, P.dtype, P.BH, st, ev ? ev + 1 : nullptr),
+                             P.g.S, P.g.d, P.dtype, P.BH, st, ev ? ev + 1 : nullptr,
+                             side ? side->fork : nullptr),
          "attention_backward");
   lh::BcastArgs a{};
   a.src[0] = dqs;
@@ -714,6 +779,21 @@ static lh_status run_backward(const Plan& P, const void* dout, const lh_buffers*
   a.shift = 0;  // the pooling adjoint: spans, in either scatter reading
   a.lout = P.tin;
   a.g = P.g;
+  if (side) {
+    // dq on the side stream once the dQ pass is done; dk, dv here after the
+    // key-block pass; then `st` waits for the side stream
+    lh::BcastArgs aq = a, akv = a;
+    akv.src[0] = dks;
+    akv.src[1] = dvs;
+    akv.out[0] = dk;
+    akv.out[1] = dv;
+    LH_HIP(hipStreamWaitEvent(side->s, side->fork, 0), "hipStreamWaitEvent");
+    LH_HIP(lh::launch_bcast(aq, P.dtype, 1, P.BH, side->s), "gather_backward");
+    LH_HIP(hipEventRecord(side->join, side->s), "hipEventRecord");
+    LH_HIP(lh::launch_bcast(akv, P.dtype, 2, P.BH, st), "gather_backward");
+    LH_HIP(hipStreamWaitEvent(st, side->join, 0), "hipStreamWaitEvent");
+    return LH_OK;
+  }
   LH_HIP(lh::launch_bcast(a, P.dtype, 3, P.BH, st), "gather_backward");
   if (ev) LH_HIP(hipEventRecord(ev[4], st), "event");
   return LH_OK;

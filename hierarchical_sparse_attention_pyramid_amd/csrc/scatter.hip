@@ -341,6 +341,7 @@ hipError_t launch_bcast(const BcastArgs& a, int dtype, int ntensors, int64_t BH,
   const int64_t nv = (int64_t)a.g.N + a.shift;  // virtual tokens
   // the shift is a template parameter: the span reading's kernels carry no
   // virtual-token bookkeeping at all
+  if (ntensors < 1 || ntensors > 3) return hipErrorInvalidValue;
   if (a.shift != 0 && (ntensors != 1 || a.mean == 0)) return hipErrorInvalidValue;
   if (LH_BC_FAST && a.g.log2p >= 2) {
     const int64_t bt = (int64_t)rgs * kFastTok;
@@ -358,10 +359,12 @@ hipError_t launch_bcast(const BcastArgs& a, int dtype, int ntensors, int64_t BH,
   const dim3 grid((unsigned)((nv + per_block - 1) / per_block), (unsigned)BH);
   if (dtype == 1) {
     if (ntensors == 3) bcast_kernel<__bf16, 3, 0><<<grid, 256, 0, st>>>(a);
+    else if (ntensors == 2) bcast_kernel<__bf16, 2, 0><<<grid, 256, 0, st>>>(a);
     else if (a.shift) bcast_kernel<__bf16, 1, 1><<<grid, 256, 0, st>>>(a);
     else bcast_kernel<__bf16, 1, 0><<<grid, 256, 0, st>>>(a);
   } else {
     if (ntensors == 3) bcast_kernel<float, 3, 0><<<grid, 256, 0, st>>>(a);
+    else if (ntensors == 2) bcast_kernel<float, 2, 0><<<grid, 256, 0, st>>>(a);
     else if (a.shift) bcast_kernel<float, 1, 1><<<grid, 256, 0, st>>>(a);
     else bcast_kernel<float, 1, 0><<<grid, 256, 0, st>>>(a);
   }

@@ -260,7 +260,14 @@ lh_status lh_gather_backward(const lh_shape *shape, const float *dqs, const floa
 
 /* a7..a9 in one call, from the buffers lh_forward filled (pos, qs, ks, vs,
  * os, lse are read).  dout: [B,H,N,d]; dq,dk,dv: [B,H,N,d] dtype.
- * ws: ws_backward bytes. */
+ * ws: ws_backward bytes.
+ * With bf16 and d = 64 the call forks part of its work onto a side stream
+ * that the library keeps per host thread and device (made by the first such
+ * call that is not inside a graph capture, kept until the process ends):
+ * the gather backward of dq runs there beside the dK/dV pass, and `stream`
+ * waits for it before the call's last work, so the outputs are ready, as
+ * always, when `stream` reaches that point.  Under graph capture the side
+ * stream joins the capture and rejoins `stream` within the call. */
 lh_status lh_backward(const lh_shape *shape, const void *dout, const lh_buffers *bufs,
                       void *dq, void *dk, void *dv, void *ws, size_t ws_bytes,
                       void *stream);
