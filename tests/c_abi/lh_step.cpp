@@ -13,6 +13,7 @@
 
 #include <cstdint>
 #include <cstdio>
+#include <string>
 #include <vector>
 
 #include "lighthouse.h"
@@ -42,8 +43,10 @@ struct Dev {
 }  // namespace
 
 int main(int argc, char** argv) {
-  if (argc != 3) {
-    std::fprintf(stderr, "usage: %s IN OUT\n", argv[0]);
+  // optional third argument "null": run on the default (NULL) stream
+  const bool null_stream = argc == 4 && std::string(argv[3]) == "null";
+  if (argc != 3 && !null_stream) {
+    std::fprintf(stderr, "usage: %s IN OUT [null]\n", argv[0]);
     return 1;
   }
   FILE* fin = std::fopen(argv[1], "rb");
@@ -104,11 +107,11 @@ int main(int argc, char** argv) {
   b.os = static_cast<float*>(os.p);
   b.lse = static_cast<float*>(lse.p);
   hipStream_t st = nullptr;
-  if (!hip_ok(hipStreamCreate(&st), "hipStreamCreate")) return 1;
+  if (!null_stream && !hip_ok(hipStreamCreate(&st), "hipStreamCreate")) return 1;
   ok = lh_ok(lh_forward(&s, q.p, k.p, v.p, out.p, &b, ws.p, wsb, st), "lh_forward") &&
        lh_ok(lh_backward(&s, dout.p, &b, dq.p, dk.p, dv.p, ws.p, wsb, st), "lh_backward") &&
        hip_ok(hipStreamSynchronize(st), "hipStreamSynchronize");
-  (void)hipStreamDestroy(st);
+  if (st) (void)hipStreamDestroy(st);
   if (!ok) return 1;
 
   FILE* fo = std::fopen(argv[2], "wb");

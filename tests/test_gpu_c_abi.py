@@ -23,16 +23,19 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 STEP = os.path.join(ROOT, "tests", "c_abi", "lh_step")
 
 CASES = [
-    # name, B, H, N, d, p, L, S, dtype
-    ("c_abi_bf16", 1, 2, 2048, 128, 4, 4, 300, "bf16"),
-    ("c_abi_fp32", 2, 1, 1024, 64, 2, 5, 150, "fp32"),
+    # name, B, H, N, d, p, L, S, dtype, stream ("own": a created stream, "null": the default one)
+    ("c_abi_bf16", 1, 2, 2048, 128, 4, 4, 300, "bf16", "own"),
+    ("c_abi_fp32", 2, 1, 1024, 64, 2, 5, 150, "fp32", "own"),
+    # bf16 at d = 64: lh_backward forks the dq gather backward onto its side stream
+    ("c_abi_bf16_d64", 1, 2, 4096, 64, 4, 4, 400, "bf16", "own"),
+    ("c_abi_bf16_d64_null_stream", 1, 2, 4096, 64, 4, 4, 400, "bf16", "null"),
 ]
 
 
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
 def test_standalone_c_program_matches_oracle(case, tmp_path, gpu_lib):
     assert os.path.exists(STEP), f"{STEP} is missing: build with hierarchical_sparse_attention_pyramid_amd/build.py"
-    name, B, H, N, d, p, L, S, dt = case
+    name, B, H, N, d, p, L, S, dt, stream = case
     print(f"[c-abi] {name}", flush=True)
     seed = 700 + CASES.index(case)
     host = {}
@@ -45,7 +48,8 @@ def test_standalone_c_program_matches_oracle(case, tmp_path, gpu_lib):
         np.array([B, H, N, d, p, L, S, 1 if dt == "bf16" else 0], np.int64).tofile(f)
         for t in ("q", "k", "v", "dout"):
             np.ascontiguousarray(host[t]).tofile(f)
-    r = subprocess.run([STEP, str(inp), str(outp)], capture_output=True, text=True, timeout=120)
+    args = [STEP, str(inp), str(outp)] + (["null"] if stream == "null" else [])
+    r = subprocess.run(args, capture_output=True, text=True, timeout=120)
     assert r.returncode == 0, f"lh_step failed: {r.stdout}\n{r.stderr}"
 
     sizes = O.level_sizes(N, p, L)
