@@ -28,7 +28,9 @@
  *    indices < N are tokens.
  *  - `stream` is a hipStream_t (NULL = the default stream).  Every call only
  *    enqueues work on that stream and returns without synchronising; outputs
- *    are ready when the stream reaches that point.
+ *    are ready when the stream reaches that point.  (lh_backward may also
+ *    run part of its work on a side stream of the library, which that stream
+ *    waits for within the call; see lh_backward.)
  *  - Inputs and outputs of one call must not overlap.
  *  - Errors: shapes and pointers are checked on the host before anything is
  *    launched.  A failed check returns LH_EINVAL / LH_EUNSUPPORTED /
