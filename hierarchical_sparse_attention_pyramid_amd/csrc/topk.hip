@@ -229,6 +229,9 @@ __global__ __launch_bounds__(kSmallThreads) void topk_small(const float* score, 
 
 // Clears words [kHdr, kZeroEnd) of every head (lh_topk only; in lh_forward
 // the pooling kernel does it).
+// workgroups per head of topk_zero: about one 16-byte store per thread
+constexpr int kZeroBlocks = ((kZeroEnd - kHdr) / 4 + kThreads - 1) / kThreads;
+
 __global__ __launch_bounds__(kThreads) void topk_zero(void* ws, int64_t stride) {
   constexpr int kVec = (kZeroEnd - kHdr) / 4;
   uint4* z = reinterpret_cast<uint4*>(head_ws(ws, blockIdx.y, stride) + kHdr);
@@ -475,7 +478,7 @@ int64_t topk_hist_stride(int64_t C) { return topk_small_path(C) ? 0 : head_strid
 
 hipError_t launch_topk_zero(void* ws, int64_t C, int64_t BH, hipStream_t st) {
   if (topk_small_path(C)) return hipSuccess;
-  topk_zero<<<dim3(16, (unsigned)BH), kThreads, 0, st>>>(ws, head_stride(C));
+  topk_zero<<<dim3(kZeroBlocks, (unsigned)BH), kThreads, 0, st>>>(ws, head_stride(C));
   return hipGetLastError();
 }
 
@@ -493,7 +496,7 @@ hipError_t launch_topk(const float* score, int32_t* sel, void* ws, const Geo& g,
   // kMaxSub slices per workgroup (16-bit LDS counters)
   const int64_t want = std::max<int64_t>(1, (LH_TOPK_WG + BH - 1) / BH);
   if (!counted) {
-    topk_zero<<<dim3(16, (unsigned)BH), kThreads, 0, st>>>(ws, stride);
+    topk_zero<<<dim3(kZeroBlocks, (unsigned)BH), kThreads, 0, st>>>(ws, stride);
     const int64_t hb0 =
         std::min<int64_t>(nsl, std::max<int64_t>(want, (nsl + kMaxSub - 1) / kMaxSub));
     const int64_t nsub0 = (nsl + hb0 - 1) / hb0;
