@@ -21,21 +21,71 @@ namespace {
 
 constexpr int kRows = 64;  // rows per workgroup and per LDS tile
 
+// x from the lane of this quad that the DPP quad permutation Ctl names
+// (0xB1: lane ^ 1, 0x4E: lane ^ 2), both 32-bit halves moved in registers.
+template <int Ctl>
+__device__ __forceinline__ double quad_swap(double x) {
+  const int lo = __builtin_amdgcn_mov_dpp(__double2loint(x), Ctl, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_mov_dpp(__double2hiint(x), Ctl, 0xF, 0xF, false);
+  return __hiloint2double(hi, lo);
+}
+
+// q.k of one row: each of the row's four lanes (an aligned quad, all active
+// together) sums its d/4 products, then the four partial sums are added.
 template <int D>
 __device__ __forceinline__ double dot4(const float (&a)[D / 4], const float* b) {
   double s = 0.0;
 #pragma unroll
   for (int e = 0; e < D / 4; ++e) s = fma((double)a[e], (double)b[e], s);
-  s += __shfl_xor(s, 1);
-  s += __shfl_xor(s, 2);
+  s += quad_swap<0xB1>(s);
+  s += quad_swap<0x4E>(s);
   return s;
 }
 
+// Rows [r0, r0 + kRows) of two [S][D] tensors into LDS (rows >= S as
+// zeros): 16-byte loads, every one of both tiles issued before the first LDS
+// store, so a pair of tiles costs one memory latency rather than one per
+// element.
 template <int D>
-__device__ __forceinline__ void stage(float* dst, const float* src, int S, int r0, int tid) {
-  for (int i = tid; i < kRows * D; i += 256) {
-    const int r = i / D;
-    dst[i] = r0 + r < S ? src[(int64_t)(r0 + r) * D + (i % D)] : 0.f;
+__device__ __forceinline__ void stage(float* dst0, const float* src0, float* dst1, const float* src1,
+                                      int S, int r0, int tid) {
+  constexpr int kPer = kRows * D / 4 / 256;  // 16-byte chunks per thread and tile
+  float4 v[2][kPer];
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const int c = tid + k * 256;  // chunk of the tile: row c / (D / 4)
+    const int r = c / (D / 4);
+    const int64_t o = (int64_t)min(r0 + r, S - 1) * D;  // clamped: never read past the end
+    const bool in = r0 + r < S;
+    v[0][k] = reinterpret_cast<const float4*>(src0 + o)[c % (D / 4)];
+    v[1][k] = reinterpret_cast<const float4*>(src1 + o)[c % (D / 4)];
+    if (!in) v[0][k] = v[1][k] = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    reinterpret_cast<float4*>(dst0)[tid + k * 256] = v[0][k];
+    reinterpret_cast<float4*>(dst1)[tid + k * 256] = v[1][k];
+  }
+}
+
+// This lane's quarter of a row (d/4 consecutive floats, 16-byte loads; src
+// must point into the tensor), replaced by zeros when !ok (a row past the
+// end: callers pass the last row's address then).
+template <int N>
+__device__ __forceinline__ void load_quarter(const float* src, bool ok, float (&x)[N]) {
+  static_assert(N % 4 == 0, "whole 16-byte chunks");
+  float4 v[N / 4];
+#pragma unroll
+  for (int i = 0; i < N / 4; ++i) v[i] = reinterpret_cast<const float4*>(src)[i];  // src is a valid row
+#pragma unroll
+  for (int i = 0; i < N / 4; ++i)
+    if (!ok) v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int i = 0; i < N / 4; ++i) {
+    x[4 * i] = v[i].x;
+    x[4 * i + 1] = v[i].y;
+    x[4 * i + 2] = v[i].z;
+    x[4 * i + 3] = v[i].w;
   }
 }
 
@@ -58,29 +108,41 @@ __global__ __launch_bounds__(256) void attn_fwd_f32(const float* __restrict__ Q,
   const int query = blockIdx.x * kQ + tid / (4 * kSplit);
   float q[D / 4];
   double o[D / 4];
+  load_quarter(Q + off + (int64_t)min(query, S - 1) * D + sub * (D / 4), query < S, q);
 #pragma unroll
-  for (int e = 0; e < D / 4; ++e) {
-    q[e] = query < S ? Q[off + (int64_t)query * D + sub * (D / 4) + e] : 0.f;
-    o[e] = 0.0;
-  }
+  for (int e = 0; e < D / 4; ++e) o[e] = 0.0;
   double m = -1e300, l = 0.0;
   const int kend = min(S, (int)(blockIdx.x + 1) * kQ);
   for (int k0 = 0; k0 < kend; k0 += kRows) {
     __syncthreads();
-    stage<D>(sK, K + off, S, k0, tid);
-    stage<D>(sV, V + off, S, k0, tid);
+    stage<D>(sK, K + off, sV, V + off, S, k0, tid);
     __syncthreads();
-    for (int jj = 0; jj < kRows / kSplit; ++jj) {
-      const int j = jj * kSplit + grp;
-      const double s = dot4<D>(q, sK + j * D + sub * (D / 4)) * scale;
-      if (k0 + j > query) continue;
-      const double mn = fmax(m, s);
-      const double alpha = expf((float)(m - mn));
-      const double p = expf((float)(s - mn));
-      l = l * alpha + p;
+    // the group's keys of this tile: scores first (independent), then one
+    // update of the running maximum, then the weights (independent)
+    constexpr int kJ = kRows / kSplit;
+    double sc[kJ];
+    double mt = m;
 #pragma unroll
-      for (int e = 0; e < D / 4; ++e) o[e] = o[e] * alpha + p * (double)sV[j * D + sub * (D / 4) + e];
-      m = mn;
+    for (int jj = 0; jj < kJ; ++jj) {
+      const int j = jj * kSplit + grp;
+      sc[jj] = dot4<D>(q, sK + j * D + sub * (D / 4)) * scale;
+      if (k0 + j <= query) mt = fmax(mt, sc[jj]);
+    }
+    if (mt > m) {
+      const double alpha = expf((float)(m - mt));
+      l *= alpha;
+#pragma unroll
+      for (int e = 0; e < D / 4; ++e) o[e] *= alpha;
+      m = mt;
+    }
+#pragma unroll
+    for (int jj = 0; jj < kJ; ++jj) {
+      const int j = jj * kSplit + grp;
+      if (k0 + j > query) continue;
+      const double p = expf((float)(sc[jj] - m));
+      l += p;
+#pragma unroll
+      for (int e = 0; e < D / 4; ++e) o[e] += p * (double)sV[j * D + sub * (D / 4) + e];
     }
   }
   // merge the key groups of each query (lanes 4, 8, 16, 32 apart); a group that
@@ -114,16 +176,14 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_f32(const float* __restrict
   const int key = blockIdx.x * kRows + tid / 4;
   float k[D / 4], v[D / 4];
   double dk[D / 4], dv[D / 4];
+  const int64_t krow = off + (int64_t)min(key, S - 1) * D + sub * (D / 4);
+  load_quarter(K + krow, key < S, k);
+  load_quarter(V + krow, key < S, v);
 #pragma unroll
-  for (int e = 0; e < D / 4; ++e) {
-    k[e] = key < S ? K[off + (int64_t)key * D + sub * (D / 4) + e] : 0.f;
-    v[e] = key < S ? V[off + (int64_t)key * D + sub * (D / 4) + e] : 0.f;
-    dk[e] = dv[e] = 0.0;
-  }
+  for (int e = 0; e < D / 4; ++e) dk[e] = dv[e] = 0.0;
   for (int q0 = blockIdx.x * kRows; q0 < S; q0 += kRows) {
     __syncthreads();
-    stage<D>(sQ, Q + off, S, q0, tid);
-    stage<D>(sG, dO + off, S, q0, tid);
+    stage<D>(sQ, Q + off, sG, dO + off, S, q0, tid);
     if (tid < kRows) {
       sL[tid] = q0 + tid < S ? LSE[blockIdx.y * (int64_t)S + q0 + tid] : 0.f;
       sDl[tid] = q0 + tid < S ? DELTA[blockIdx.y * (int64_t)S + q0 + tid] : 0.f;
@@ -165,19 +225,17 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_f32(const float* __restrict__
   const int query = blockIdx.x * kRows + tid / 4;
   float q[D / 4], g[D / 4];
   double dq[D / 4];
+  const int64_t qrow = off + (int64_t)min(query, S - 1) * D + sub * (D / 4);
+  load_quarter(Q + qrow, query < S, q);
+  load_quarter(dO + qrow, query < S, g);
 #pragma unroll
-  for (int e = 0; e < D / 4; ++e) {
-    q[e] = query < S ? Q[off + (int64_t)query * D + sub * (D / 4) + e] : 0.f;
-    g[e] = query < S ? dO[off + (int64_t)query * D + sub * (D / 4) + e] : 0.f;
-    dq[e] = 0.0;
-  }
+  for (int e = 0; e < D / 4; ++e) dq[e] = 0.0;
   const double lse = query < S ? LSE[blockIdx.y * (int64_t)S + query] : 0.f;
   const double dl = query < S ? DELTA[blockIdx.y * (int64_t)S + query] : 0.f;
   const int kend = min(S, (int)(blockIdx.x + 1) * kRows);
   for (int k0 = 0; k0 < kend; k0 += kRows) {
     __syncthreads();
-    stage<D>(sK, K + off, S, k0, tid);
-    stage<D>(sV, V + off, S, k0, tid);
+    stage<D>(sK, K + off, sV, V + off, S, k0, tid);
     __syncthreads();
     for (int j = 0; j < kRows; ++j) {
       const float* kj = sK + j * D + sub * (D / 4);
