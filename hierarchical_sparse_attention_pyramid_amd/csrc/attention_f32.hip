@@ -163,6 +163,35 @@ __global__ __launch_bounds__(256) void attn_fwd_f32(const float* __restrict__ Q,
   if (sub == 0) LSE[blockIdx.y * (int64_t)S + query] = (float)(m + log(l));
 }
 
+// Backward passes: a row's work is split over kSplit lane groups as in the
+// forward (item j of a tile goes to group j mod kSplit), so that a short
+// sequence still yields many workgroups; the groups' float64 sums are added
+// by butterfly shuffles at the end.  A lane takes a few items of a tile at
+// a time, their dot products independent of each other.  (Two heads of 512
+// rows: dK/dV 200 -> 31 us, dQ 163 -> 26 us against one lane group per row;
+// 4 groups give 86 and 61 us, and 16 groups stay ahead at 4,096 rows.)
+template <int D>
+struct BwdCfg {
+  static constexpr int kRowsPerBlock = 256 / (4 * kSplit);
+  static constexpr int kItems = kRows / kSplit;   // items of a tile per lane group
+  static constexpr int kUdq = D == 64 ? 4 : 2;    // items at a time: dQ pass
+  static constexpr int kUdkdv = D == 64 ? 2 : 1;  // dK/dV pass (two sums per key)
+  static_assert(kItems % kUdq == 0 && kItems % kUdkdv == 0, "whole steps per tile");
+};
+
+template <int N>
+__device__ __forceinline__ void sum_groups(double (&x)[N]) {
+#pragma unroll
+  for (int w = 4; w < 4 * kSplit; w <<= 1) {
+#pragma unroll
+    for (int e = 0; e < N; ++e) x[e] += __shfl_xor(x[e], w);
+  }
+}
+
+// dK, dV: a workgroup owns kRowsPerBlock keys and walks the queries from its
+// first key to the end; a probability P = exp(s - lse) of query i and key j
+// adds P dO_i to dV_j and P (dP - delta_i) q_i to dK_j (scaled once at the
+// end).
 template <int D>
 __global__ __launch_bounds__(256) void attn_bwd_dkdv_f32(const float* __restrict__ Q, const float* __restrict__ K,
                                                          const float* __restrict__ V, const float* __restrict__ dO,
@@ -170,10 +199,12 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_f32(const float* __restrict
                                                          const float* __restrict__ DELTA,
                                                          float* __restrict__ dK, float* __restrict__ dV,
                                                          int S, double scale) {
+  using C = BwdCfg<D>;
   __shared__ float sQ[kRows * D], sG[kRows * D], sL[kRows], sDl[kRows];
-  const int tid = threadIdx.x, sub = tid & 3;
+  const int tid = threadIdx.x, sub = tid & 3, grp = (tid >> 2) % kSplit;
   const int64_t off = blockIdx.y * (int64_t)S * D;
-  const int key = blockIdx.x * kRows + tid / 4;
+  const int key0 = blockIdx.x * C::kRowsPerBlock;
+  const int key = key0 + tid / (4 * kSplit);
   float k[D / 4], v[D / 4];
   double dk[D / 4], dv[D / 4];
   const int64_t krow = off + (int64_t)min(key, S - 1) * D + sub * (D / 4);
@@ -181,7 +212,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_f32(const float* __restrict
   load_quarter(V + krow, key < S, v);
 #pragma unroll
   for (int e = 0; e < D / 4; ++e) dk[e] = dv[e] = 0.0;
-  for (int q0 = blockIdx.x * kRows; q0 < S; q0 += kRows) {
+  for (int q0 = key0; q0 < S; q0 += kRows) {
     __syncthreads();
     stage<D>(sQ, Q + off, sG, dO + off, S, q0, tid);
     if (tid < kRows) {
@@ -189,23 +220,34 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_f32(const float* __restrict
       sDl[tid] = q0 + tid < S ? DELTA[blockIdx.y * (int64_t)S + q0 + tid] : 0.f;
     }
     __syncthreads();
-    for (int i = 0; i < kRows; ++i) {
-      const float* qi = sQ + i * D + sub * (D / 4);
-      const float* gi = sG + i * D + sub * (D / 4);
-      const double s = dot4<D>(k, qi) * scale;
-      const double dp = dot4<D>(v, gi);
-      const int query = q0 + i;
-      if (query >= S || key > query) continue;
-      const double p = expf((float)(s - (double)sL[i]));
-      const double ds = p * (dp - (double)sDl[i]);
+    for (int ii = 0; ii < C::kItems; ii += C::kUdkdv) {
+      double s[C::kUdkdv], dp[C::kUdkdv];
 #pragma unroll
-      for (int e = 0; e < D / 4; ++e) {
-        dv[e] = fma(p, (double)gi[e], dv[e]);
-        dk[e] = fma(ds, (double)qi[e], dk[e]);
+      for (int u = 0; u < C::kUdkdv; ++u) {
+        const int i = (ii + u) * kSplit + grp;
+        s[u] = dot4<D>(k, sQ + i * D + sub * (D / 4)) * scale;
+        dp[u] = dot4<D>(v, sG + i * D + sub * (D / 4));
+      }
+#pragma unroll
+      for (int u = 0; u < C::kUdkdv; ++u) {
+        const int i = (ii + u) * kSplit + grp;
+        const int query = q0 + i;
+        if (query >= S || key > query) continue;
+        const float* qi = sQ + i * D + sub * (D / 4);
+        const float* gi = sG + i * D + sub * (D / 4);
+        const double p = expf((float)(s[u] - (double)sL[i]));
+        const double ds = p * (dp[u] - (double)sDl[i]);
+#pragma unroll
+        for (int e = 0; e < D / 4; ++e) {
+          dv[e] = fma(p, (double)gi[e], dv[e]);
+          dk[e] = fma(ds, (double)qi[e], dk[e]);
+        }
       }
     }
   }
-  if (key >= S) return;
+  sum_groups(dk);
+  sum_groups(dv);
+  if (key >= S || grp != 0) return;
 #pragma unroll
   for (int e = 0; e < D / 4; ++e) {
     dK[off + (int64_t)key * D + sub * (D / 4) + e] = (float)(dk[e] * scale);
@@ -213,16 +255,19 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_f32(const float* __restrict
   }
 }
 
+// dQ: a workgroup owns kRowsPerBlock queries and walks the keys up to its
+// last query; dQ_i sums P (dP - delta_i) k_j (scaled once at the end).
 template <int D>
 __global__ __launch_bounds__(256) void attn_bwd_dq_f32(const float* __restrict__ Q, const float* __restrict__ K,
                                                        const float* __restrict__ V, const float* __restrict__ dO,
                                                        const float* __restrict__ LSE,
                                                        const float* __restrict__ DELTA,
                                                        float* __restrict__ dQ, int S, double scale) {
+  using C = BwdCfg<D>;
   __shared__ float sK[kRows * D], sV[kRows * D];
-  const int tid = threadIdx.x, sub = tid & 3;
+  const int tid = threadIdx.x, sub = tid & 3, grp = (tid >> 2) % kSplit;
   const int64_t off = blockIdx.y * (int64_t)S * D;
-  const int query = blockIdx.x * kRows + tid / 4;
+  const int query = blockIdx.x * C::kRowsPerBlock + tid / (4 * kSplit);
   float q[D / 4], g[D / 4];
   double dq[D / 4];
   const int64_t qrow = off + (int64_t)min(query, S - 1) * D + sub * (D / 4);
@@ -232,22 +277,32 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_f32(const float* __restrict__
   for (int e = 0; e < D / 4; ++e) dq[e] = 0.0;
   const double lse = query < S ? LSE[blockIdx.y * (int64_t)S + query] : 0.f;
   const double dl = query < S ? DELTA[blockIdx.y * (int64_t)S + query] : 0.f;
-  const int kend = min(S, (int)(blockIdx.x + 1) * kRows);
+  const int kend = min(S, (int)(blockIdx.x + 1) * C::kRowsPerBlock);
   for (int k0 = 0; k0 < kend; k0 += kRows) {
     __syncthreads();
     stage<D>(sK, K + off, sV, V + off, S, k0, tid);
     __syncthreads();
-    for (int j = 0; j < kRows; ++j) {
-      const float* kj = sK + j * D + sub * (D / 4);
-      const double s = dot4<D>(q, kj) * scale;
-      const double dp = dot4<D>(g, sV + j * D + sub * (D / 4));
-      if (k0 + j > query) continue;
-      const double ds = (double)expf((float)(s - lse)) * (dp - dl);
+    for (int jj = 0; jj < C::kItems; jj += C::kUdq) {
+      double s[C::kUdq], dp[C::kUdq];
 #pragma unroll
-      for (int e = 0; e < D / 4; ++e) dq[e] = fma(ds, (double)kj[e], dq[e]);
+      for (int u = 0; u < C::kUdq; ++u) {
+        const int j = (jj + u) * kSplit + grp;
+        s[u] = dot4<D>(q, sK + j * D + sub * (D / 4)) * scale;
+        dp[u] = dot4<D>(g, sV + j * D + sub * (D / 4));
+      }
+#pragma unroll
+      for (int u = 0; u < C::kUdq; ++u) {
+        const int j = (jj + u) * kSplit + grp;
+        if (k0 + j > query) continue;
+        const float* kj = sK + j * D + sub * (D / 4);
+        const double ds = (double)expf((float)(s[u] - lse)) * (dp[u] - dl);
+#pragma unroll
+        for (int e = 0; e < D / 4; ++e) dq[e] = fma(ds, (double)kj[e], dq[e]);
+      }
     }
   }
-  if (query >= S) return;
+  sum_groups(dq);
+  if (query >= S || grp != 0) return;
 #pragma unroll
   for (int e = 0; e < D / 4; ++e) dQ[off + (int64_t)query * D + sub * (D / 4) + e] = (float)(dq[e] * scale);
 }
@@ -264,22 +319,29 @@ hipError_t launch_attn_fwd_f32(const float* q, const float* k, const float* v, f
   return hipGetLastError();
 }
 
+template <int D>
+static hipError_t bwd_passes(const float* q, const float* k, const float* v, const float* lse,
+                             const float* delta, const float* dout, float* dq, float* dk, float* dv,
+                             int64_t S, int64_t BH, hipStream_t st, hipEvent_t* ev) {
+  using C = BwdCfg<D>;
+  const dim3 grid((unsigned)((S + C::kRowsPerBlock - 1) / C::kRowsPerBlock), (unsigned)BH);
+  const double scale = 1.0 / sqrt((double)D);
+  attn_bwd_dkdv_f32<D><<<grid, 256, 0, st>>>(q, k, v, dout, lse, delta, dk, dv, (int)S, scale);
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess && ev) e = hipEventRecord(ev[1], st);
+  if (e != hipSuccess) return e;
+  attn_bwd_dq_f32<D><<<grid, 256, 0, st>>>(q, k, v, dout, lse, delta, dq, (int)S, scale);
+  e = hipGetLastError();
+  if (e == hipSuccess && ev) e = hipEventRecord(ev[2], st);
+  return e;
+}
+
 hipError_t launch_attn_bwd_f32(const float* q, const float* k, const float* v, const float* lse,
                                const float* delta, const float* dout, float* dq, float* dk,
                                float* dv, int64_t S, int d, int64_t BH, hipStream_t st,
                                hipEvent_t* ev) {
-  const dim3 grid((unsigned)((S + kRows - 1) / kRows), (unsigned)BH);
-  const double scale = 1.0 / sqrt((double)d);
-  if (d == 64) attn_bwd_dkdv_f32<64><<<grid, 256, 0, st>>>(q, k, v, dout, lse, delta, dk, dv, (int)S, scale);
-  else attn_bwd_dkdv_f32<128><<<grid, 256, 0, st>>>(q, k, v, dout, lse, delta, dk, dv, (int)S, scale);
-  hipError_t e = hipGetLastError();
-  if (e == hipSuccess && ev) e = hipEventRecord(ev[1], st);
-  if (e != hipSuccess) return e;
-  if (d == 64) attn_bwd_dq_f32<64><<<grid, 256, 0, st>>>(q, k, v, dout, lse, delta, dq, (int)S, scale);
-  else attn_bwd_dq_f32<128><<<grid, 256, 0, st>>>(q, k, v, dout, lse, delta, dq, (int)S, scale);
-  e = hipGetLastError();
-  if (e == hipSuccess && ev) e = hipEventRecord(ev[2], st);
-  return e;
+  return d == 64 ? bwd_passes<64>(q, k, v, lse, delta, dout, dq, dk, dv, S, BH, st, ev)
+                 : bwd_passes<128>(q, k, v, lse, delta, dout, dq, dk, dv, S, BH, st, ev);
 }
 
 }  // namespace lh
