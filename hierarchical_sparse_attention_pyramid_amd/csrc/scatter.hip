@@ -175,21 +175,39 @@ __global__ __launch_bounds__(256) void bcast_fast(BcastArgs a) {
   __shared__ int32_t soff[kMaxLevels];  // start of level l's run in sp
 
   // ---- stage positions vpos: virtual tokens [B0, B0 + BT), then each
-  // level's ancestors of them
-  for (int i = threadIdx.x; i < BT; i += 256) {
-    const int32_t t = B0 + i - SH;
-    sp[i] = (SH == 0 || t >= 0) && t < g.N ? pos[t] : -1;
-  }
+  // level's ancestors of them, one run per level (run l: max(1, BT / p^l)
+  // entries from entry B0 / p^l; at most 256 for l >= 1 since BT <= 1024 and
+  // p >= 4).  A thread issues every position load it makes before its first
+  // LDS store: the staging costs one memory latency, not one per level.
   const int lbt = __builtin_ctz(BT);  // BT is a power of two (64 tokens x 8 or 16 row groups)
-  int off = BT;
-  for (int l = 1; l < g.L; ++l) {
-    const int n = lg * l >= lbt ? 1 : BT >> (lg * l);  // ancestors of the block: max(1, BT / p^l)
-    const int32_t jlo = (B0 >> (lg * l)) - SH;
-    if (threadIdx.x == 0) soff[l] = off;
-    for (int i = threadIdx.x; i < n; i += 256)
-      sp[off + i] =
-          (SH == 0 || jlo + i >= 0) && jlo + i < g.nlev[l] ? pos[g.base[l] + jlo + i] : -1;
-    off += n;
+  {
+    constexpr int kTok = 1024 / 256;  // level-0 entries per thread
+    int32_t p0[kTok], pl[kMaxLevels];
+#pragma unroll
+    for (int k = 0; k < kTok; ++k) {
+      const int i = threadIdx.x + k * 256;
+      const int32_t t = B0 + i - SH;
+      p0[k] = i < BT && (SH == 0 || t >= 0) && t < g.N ? pos[t] : -1;
+    }
+#pragma unroll
+    for (int l = 1; l < kMaxLevels; ++l) {
+      const int n = lg * l >= lbt ? 1 : BT >> (lg * l);
+      const int32_t j = (B0 >> (lg * l)) - SH + (int)threadIdx.x;
+      pl[l] = l < g.L && (int)threadIdx.x < n && (SH == 0 || j >= 0) && j < g.nlev[l]
+                  ? pos[g.base[l] + j] : -1;
+    }
+#pragma unroll
+    for (int k = 0; k < kTok; ++k)
+      if (threadIdx.x + k * 256 < BT) sp[threadIdx.x + k * 256] = p0[k];
+    int off = BT;
+#pragma unroll
+    for (int l = 1; l < kMaxLevels; ++l) {
+      if (l >= g.L) break;
+      const int n = lg * l >= lbt ? 1 : BT >> (lg * l);
+      if (threadIdx.x == 0) soff[l] = off;
+      if ((int)threadIdx.x < n) sp[off + threadIdx.x] = pl[l];
+      off += n;
+    }
   }
   __syncthreads();
   const int32_t t0 = B0 + rg * kFastTok;
