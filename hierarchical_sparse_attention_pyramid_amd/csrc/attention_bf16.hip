@@ -20,7 +20,9 @@
 // Backward: a key-block pass (dK, dV; keys stationary) and a query-block pass
 // (dQ; queries stationary), both atomic-free, recomputing P from the stored
 // log-sum-exp.
+#include <algorithm>
 #include <type_traits>
+#include <vector>
 
 #include "kernels.h"
 
@@ -339,10 +341,28 @@ struct FwdCfg {
   static constexpr int kThreads = 64 * WAVES;
 };
 
+// Key-range split (FwdSplit::n > 0), for causal grids too small to balance:
+// the heaviest query blocks (those with more key tiles than the mean load of
+// a resident workgroup slot) each run as two workgroups, chunk 0 over the
+// first half of the block's key tiles and chunk 1 over the rest (which holds
+// the diagonal).  A chunk writes its partial result, the output normalised by
+// its own sum and lambda = m + log2(sum) per query (chunk 1 into O and LSE,
+// chunk 0 into the split buffers); attn_fwd_merge then combines the two:
+//   w_c = exp2(lambda_c - max lambda), O = (w_0 y_0 + w_1 y_1) / (w_0 + w_1).
+// order[] lists every head's work items (whole blocks and chunks) by
+// decreasing number of key tiles; workgroups take them in that order.
+constexpr int kSplitItems = 1024;
+struct FwdSplit {
+  float* o;      // [BH][S][D] chunk-0 partial outputs
+  float* lam;    // [BH][S] chunk-0 lambda (log2 units)
+  int32_t n;     // work items per head (0: no split)
+  uint16_t order[kSplitItems];  // item = query block << 2 | kind (0 whole, 1 chunk 0, 2 chunk 1)
+};
+
 template <int D, int QW, int WAVES, int MINW>
 __global__ __launch_bounds__(64 * WAVES, MINW) void attn_fwd_bf16(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
-    float* __restrict__ O, float* __restrict__ LSE, int S, float sl2, int paired) {
+    float* __restrict__ O, float* __restrict__ LSE, int S, float sl2, int paired, FwdSplit sp) {
   using C = FwdCfg<D, QW, WAVES>;
   constexpr int NQB = C::kNQB;
   __shared__ __attribute__((aligned(1024))) __bf16 sKV[2][2][C::kTile];  // [buffer][K,V]
@@ -351,11 +371,16 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void attn_fwd_bf16(
   const int h = lane >> 5, c32 = lane & 31;
   const uint32_t lrow = lane_rows<D>(lane), ltr = lane_tr<D>(lane);
   const int nqb = (S + C::kQB - 1) / C::kQB;
-  const Runs runs = plan_runs(blockIdx.x, gridDim.x, nqb, paired);
+  const bool split = sp.n > 0;
+  const Runs runs = plan_runs(blockIdx.x, gridDim.x, split ? sp.n : nqb, split ? 0 : paired);
   const int64_t bh = __builtin_amdgcn_readfirstlane(runs.head);
   for (int run = 0; run < runs.n; ++run) {
   if (run > 0) __syncthreads();  // every wave is done with the LDS tiles
-  const int qblk = nqb - 1 - __builtin_amdgcn_readfirstlane(runs.rank[run]);
+  const int rank = __builtin_amdgcn_readfirstlane(runs.rank[run]);
+  // split: the rank-th item of the list (kind 0 whole block, 1 chunk 0, 2 chunk 1)
+  const int code = split ? (int)sp.order[rank] : 0;
+  const int qblk = split ? code >> 2 : nqb - 1 - rank;
+  const int kind = code & 3;
   const int q0 = qblk * C::kQB;
   const int qw0 = q0 + wave * C::kQW;
   const __bf16* Qh = Q + bh * (int64_t)S * D;
@@ -363,9 +388,13 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void attn_fwd_bf16(
   const __bf16* Vh = V + bh * (int64_t)S * D;
 
   const int kend = min(S, q0 + C::kQB);
-  const int ntiles = (kend + C::kKT - 1) / C::kKT;
-  load_tile<D, C::kKT, WAVES>(Kh, S, 0, sKV[0][0], wave, lane);
-  load_tile<D, C::kKT, WAVES>(Vh, S, 0, sKV[0][1], wave, lane);
+  const int nall = (kend + C::kKT - 1) / C::kKT;
+  const int kt0 = kind == 2 ? nall >> 1 : 0;        // this workgroup's key tiles
+  const int ntiles = kind == 1 ? nall >> 1 : nall;  // [kt0, ntiles)
+  if (kt0 < ntiles) {
+    load_tile<D, C::kKT, WAVES>(Kh, S, kt0 * C::kKT, sKV[kt0 & 1][0], wave, lane);
+    load_tile<D, C::kKT, WAVES>(Vh, S, kt0 * C::kKT, sKV[kt0 & 1][1], wave, lane);
+  }
 
   bf16x8 qreg[NQB][D / 16];
 #pragma unroll
@@ -388,7 +417,7 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void attn_fwd_bf16(
     lsum[qb] = 0.f;
   }
 
-  for (int kt = 0; kt < ntiles; ++kt) {
+  for (int kt = kt0; kt < ntiles; ++kt) {
     const int k0 = kt * C::kKT;
     wait_loads();
     __syncthreads();  // tile kt is in LDS; buffer (kt+1)&1 is free
@@ -477,13 +506,18 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void attn_fwd_bf16(
     }
   }
 
+  float* Oh = O + bh * (int64_t)S * D;
+  float* Lh = LSE + bh * (int64_t)S;
   if (qw0 < S) {
-    float* Oh = O + bh * (int64_t)S * D;
-    float* Lh = LSE + bh * (int64_t)S;
+    // kind 1 writes to the split buffers; kinds 1 and 2 write partials
+    float* dO_ = kind == 1 ? sp.o + bh * (int64_t)S * D : Oh;
+    float* dL = kind == 1 ? sp.lam + bh * (int64_t)S : Lh;
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
       const float lt = lsum[qb] + __shfl_xor(lsum[qb], 32);
-      const float inv = 1.0f / lt;
+      // a chunk that saw none of the query's keys holds an empty partial
+      const float inv = kind == 0 || lt > 0.f ? 1.0f / lt : 0.f;
+      const float lam = kind == 0 || lt > 0.f ? mrow[qb] + log2f(lt) : neg_inf();
       const int query = qw0 + qb * 32 + c32;
       if (query < S) {
 #pragma unroll
@@ -493,13 +527,42 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void attn_fwd_bf16(
             f32x4 o;
 #pragma unroll
             for (int r = 0; r < 4; ++r) o[r] = oacc[qb][mb][4 * j + r] * inv;
-            *reinterpret_cast<f32x4*>(Oh + (int64_t)query * D + mb * 32 + 8 * j + 4 * h) = o;
+            *reinterpret_cast<f32x4*>(dO_ + (int64_t)query * D + mb * 32 + 8 * j + 4 * h) = o;
           }
-        if (h == 0) Lh[query] = (mrow[qb] + log2f(lt)) * kLn2;
+        if (h == 0) dL[query] = kind == 0 ? lam * kLn2 : lam;
       }
     }
   }
   }  // run
+}
+
+// Combines the two chunks of every split query block (rows [r0, S) of each
+// head, the blocks from the first split one on): chunk 0's partial from the
+// split buffers, chunk 1's from O and LSE (lambda in log2 units), both
+// written by attn_fwd_bf16; writes the final O and the natural-log LSE.
+template <int D>
+__global__ __launch_bounds__(256) void attn_fwd_merge(float* __restrict__ O, float* __restrict__ LSE,
+                                                      const float* __restrict__ P0,
+                                                      const float* __restrict__ L0, int S, int r0) {
+  constexpr int kLanes = D / 4, kRows = 256 / kLanes;
+  const int64_t bh = blockIdx.y;
+  const int row = r0 + (int)blockIdx.x * kRows + (int)threadIdx.x / kLanes;
+  const int lane = threadIdx.x % kLanes;
+  if (row >= S) return;
+  const int64_t ri = bh * (int64_t)S + row;
+  const float l0 = L0[ri], l1 = LSE[ri];
+  const float lm = fmaxf(l0, l1);  // finite: one chunk holds the query's own key
+  const float w0 = fexp2(l0 - lm), w1 = fexp2(l1 - lm);
+  const float wt = w0 + w1;
+  const float inv = 1.0f / wt;
+  const int64_t at = ri * D + 4 * lane;
+  const f32x4 y0 = *reinterpret_cast<const f32x4*>(P0 + at);
+  const f32x4 y1 = *reinterpret_cast<const f32x4*>(O + at);
+  f32x4 o;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) o[r] = (w0 * y0[r] + w1 * y1[r]) * inv;
+  *reinterpret_cast<f32x4*>(O + at) = o;
+  if (lane == 0) LSE[ri] = (lm + log2f(wt)) * kLn2;
 }
 
 // ------------------------------------------------------------------ backward
@@ -968,8 +1031,93 @@ hipError_t launch_attn_bwd_f32(const float* q, const float* k, const float* v, c
                                float* dv, int64_t S, int d, int64_t BH, hipStream_t st,
                                hipEvent_t* ev);
 
+namespace {
+// Workgroups of the forward kernel resident at once on the current device
+// (compute units x workgroups per unit), looked up once per device.
+template <typename Kern>
+int64_t resident_slots(Kern kern, int threads) {
+  static int64_t cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cache[dev] == 0) {
+    int cus = 0, per = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kern, threads, 0) != hipSuccess)
+      return 0;
+    cache[dev] = (int64_t)cus * per;
+  }
+  return cache[dev];
+}
+
+#ifndef LH_FWD_SPLIT
+#define LH_FWD_SPLIT 1
+#endif
+
+// The split plan of a causal forward grid that fits in one round of the
+// resident workgroup slots (grids with more workgroups than slots balance
+// well enough by themselves: at 16 heads of 8,192 rows, 1.33 workgroups per
+// slot, the split measured 3% slower, while at 16 heads of 4,096 rows and
+// d = 128, one workgroup per slot, the forward went 0.125 -> 0.108 ms).
+// Blocks with more key tiles than the mean load per slot (total tiles /
+// slots) run as two chunks.  Fills sp.n and sp.order (items by decreasing
+// tiles, ties by block, then kind); returns the first split block (nb if none).
+int64_t plan_split(int64_t S, int64_t nb, int qb, int64_t BH, int64_t slots, FwdSplit& sp) {
+  sp.n = 0;
+  if (!LH_FWD_SPLIT || slots <= 0 || nb < 2 || nb * BH > slots) return nb;
+  auto tiles = [&](int64_t b) { return (std::min<int64_t>(S, (b + 1) * qb) + 63) / 64; };
+  int64_t total = 0;
+  for (int64_t b = 0; b < nb; ++b) total += tiles(b);
+  const int64_t mean = (total * BH + slots - 1) / slots;
+  int64_t b0 = nb;  // tiles(b) is nondecreasing: the split blocks are a suffix
+  while (b0 > 0 && tiles(b0 - 1) > mean && tiles(b0 - 1) >= 2) --b0;
+  if (b0 == nb || nb + (nb - b0) > kSplitItems || nb >= (1 << 14)) return nb;
+  struct Item { int64_t w; int code; };
+  std::vector<Item> it;
+  for (int64_t b = 0; b < nb; ++b) {
+    const int64_t t = tiles(b);
+    if (b < b0) {
+      it.push_back({t, (int)(b << 2)});
+    } else {
+      it.push_back({t >> 1, (int)(b << 2 | 1)});
+      it.push_back({t - (t >> 1), (int)(b << 2 | 2)});
+    }
+  }
+  std::stable_sort(it.begin(), it.end(), [](const Item& x, const Item& y) {
+    return x.w != y.w ? x.w > y.w : x.code > y.code;
+  });
+  sp.n = (int32_t)it.size();
+  for (size_t i = 0; i < it.size(); ++i) sp.order[i] = (uint16_t)it[i].code;
+  return b0;
+}
+
+template <int D, int QW, int WAVES, int MINW>
+hipError_t fwd_bf16(const __bf16* Q, const __bf16* K, const __bf16* V, float* o, float* lse,
+                    int64_t S, int64_t BH, float sl2, const FwdSplitBufs* sb, hipStream_t st) {
+  using C = FwdCfg<D, QW, WAVES>;
+  auto kern = attn_fwd_bf16<D, QW, WAVES, MINW>;
+  const int64_t nb = (S + C::kQB - 1) / C::kQB;
+  FwdSplit sp;
+  sp.o = sb ? sb->o : nullptr;
+  sp.lam = sb ? sb->lam : nullptr;
+  int64_t b0 = nb;
+  if (sb) b0 = plan_split(S, nb, C::kQB, BH, resident_slots(kern, C::kThreads), sp);
+  else sp.n = 0;
+  const bool pr = sp.n == 0 && LH_PAIR_FWD && pair_blocks(nb, BH);
+  const int64_t grid = sp.n > 0 ? sp.n * BH : causal_grid(nb, BH, pr);
+  kern<<<dim3((unsigned)grid), C::kThreads, 0, st>>>(Q, K, V, o, lse, (int)S, sl2, pr ? 1 : 0, sp);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || sp.n == 0) return e;
+  const int64_t r0 = b0 * C::kQB;  // first row of the split blocks
+  constexpr int kRows = 256 / (D / 4);
+  attn_fwd_merge<D><<<dim3((unsigned)((S - r0 + kRows - 1) / kRows), (unsigned)BH), 256, 0, st>>>(
+      o, lse, sp.o, sp.lam, (int)S, (int)r0);
+  return hipGetLastError();
+}
+}  // namespace
+
 hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, float* o, float* lse,
-                           int64_t S, int d, int dtype, int64_t BH, hipStream_t st) {
+                           int64_t S, int d, int dtype, int64_t BH, hipStream_t st,
+                           const FwdSplitBufs* split) {
   if (S == 0) return hipSuccess;
   if (dtype == 0)
     return launch_attn_fwd_f32(static_cast<const float*>(q), static_cast<const float*>(k),
@@ -978,22 +1126,11 @@ hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, float* o
   const auto Q = static_cast<const __bf16*>(q);
   const auto K = static_cast<const __bf16*>(k);
   const auto V = static_cast<const __bf16*>(v);
-  if (d == 64) {
-    using C = FwdCfg<64, LH_FWD64_QW, LH_FWD64_WAVES>;
-    const int64_t nb = (S + C::kQB - 1) / C::kQB;
-    const bool pr = LH_PAIR_FWD && pair_blocks(nb, BH);
-    attn_fwd_bf16<64, LH_FWD64_QW, LH_FWD64_WAVES, LH_FWD64_MINW>
-        <<<dim3((unsigned)causal_grid(nb, BH, pr)), C::kThreads, 0, st>>>(Q, K, V, o, lse, (int)S,
-                                                                          sl2, pr ? 1 : 0);
-  } else {
-    using C = FwdCfg<128, LH_FWD128_QW, LH_FWD128_WAVES>;
-    const int64_t nb = (S + C::kQB - 1) / C::kQB;
-    const bool pr = LH_PAIR_FWD && pair_blocks(nb, BH);
-    attn_fwd_bf16<128, LH_FWD128_QW, LH_FWD128_WAVES, LH_FWD128_MINW>
-        <<<dim3((unsigned)causal_grid(nb, BH, pr)), C::kThreads, 0, st>>>(Q, K, V, o, lse, (int)S,
-                                                                          sl2, pr ? 1 : 0);
-  }
-  return hipGetLastError();
+  if (d == 64)
+    return fwd_bf16<64, LH_FWD64_QW, LH_FWD64_WAVES, LH_FWD64_MINW>(Q, K, V, o, lse, S, BH, sl2,
+                                                                     split, st);
+  return fwd_bf16<128, LH_FWD128_QW, LH_FWD128_WAVES, LH_FWD128_MINW>(Q, K, V, o, lse, S, BH, sl2,
+                                                                       split, st);
 }
 
 hipError_t launch_attn_bwd(const void* q, const void* k, const void* v, const float* o,

@@ -90,8 +90,16 @@ hipError_t launch_gather(const int32_t* sel, const void* const q[3], const Lay& 
                          void* const qs[3], const Geo& g, int dtype, int64_t BH, hipStream_t st);
 
 // attention
+// Buffers of the forward's key-range split (bf16): chunk-0 partial outputs
+// [BH][S][d] and lambdas [BH][S], float32.  The split runs only on causal
+// grids too small to balance (see attn_fwd_bf16).
+struct FwdSplitBufs {
+  float* o;
+  float* lam;
+};
 hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, float* o, float* lse,
-                           int64_t S, int d, int dtype, int64_t BH, hipStream_t st);
+                           int64_t S, int d, int dtype, int64_t BH, hipStream_t st,
+                           const FwdSplitBufs* split = nullptr);
 hipError_t launch_attn_bwd(const void* q, const void* k, const void* v, const float* o,
                            const float* lse, const void* dout, float* dq, float* dk, float* dv,
                            float* delta, float* lse2, int64_t S, int d, int dtype, int64_t BH,

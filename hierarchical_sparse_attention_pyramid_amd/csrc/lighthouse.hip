@@ -256,7 +256,10 @@ lh_status make_plan(const lh_shape* s, Plan& P) {
   z.ws_scatter_backward = sums1;
   // the pooling pass clears the top-K histograms while it writes its float32
   // sums: the two regions must not overlap
-  z.ws_forward = align_up(z.ws_build_pyramid) + z.ws_topk;
+  // after the top-K the region is reused by the attention's key-range split
+  // (chunk-0 outputs and lambdas; bf16 only)
+  const size_t split = s->dtype == LH_BF16 ? align_up(z.bytes_sub_f32) + align_up(z.bytes_lse) : 0;
+  z.ws_forward = std::max(align_up(z.ws_build_pyramid) + z.ws_topk, split);
   z.ws_backward = align_up(z.bytes_sub) + 3 * align_up(z.bytes_sub_f32) + z.ws_attention_backward +
                   z.ws_scatter_backward;
   return LH_OK;
@@ -547,7 +550,11 @@ static lh_status run_forward(const Plan& P, const void* q, const void* k, const 
   LH_HIP(lh::launch_gather(b->sel, lv0, P.tin, pyr, b->sub_idx, b->pos, sub, P.g, P.dtype, P.BH, st),
          "gather");
   if (ev) LH_HIP(hipEventRecord(ev[2], st), "event");
-  LH_HIP(lh::launch_attn_fwd(b->qs, b->ks, b->vs, b->os, b->lse, P.g.S, P.g.d, P.dtype, P.BH, st),
+  // the attention's split buffers: the start of ws, free once the top-K is done
+  lh::FwdSplitBufs sb{static_cast<float*>(ws),
+                      reinterpret_cast<float*>(static_cast<char*>(ws) + align_up(P.sz.bytes_sub_f32))};
+  LH_HIP(lh::launch_attn_fwd(b->qs, b->ks, b->vs, b->os, b->lse, P.g.S, P.g.d, P.dtype, P.BH, st,
+                             P.dtype == LH_BF16 ? &sb : nullptr),
          "attention");
   if (ev) LH_HIP(hipEventRecord(ev[3], st), "event");
   lh::BcastArgs a{};

@@ -230,7 +230,11 @@ lh_status lh_scatter(const lh_shape *shape, const float *os, const int32_t *pos,
 
 /* a1..a6 in one call.  bufs: every field required; out: [B,H,N,d].
  * ws: ws_forward bytes.  Causal in the tokens only with
- * shape->scatter = LH_SCATTER_CAUSAL (see lh_scatter_mode). */
+ * shape->scatter = LH_SCATTER_CAUSAL (see lh_scatter_mode).
+ * With bf16 on grids small enough to leave the GPU's workgroup slots
+ * unevenly loaded, the attention splits the key range of its heaviest query
+ * blocks in two and merges the halves (partials in ws), so os and lse can
+ * differ from lh_attention's in the last bits. */
 lh_status lh_forward(const lh_shape *shape, const void *q, const void *k, const void *v,
                      void *out, const lh_buffers *bufs, void *ws, size_t ws_bytes,
                      void *stream);

@@ -63,3 +63,42 @@ def test_attention_entry_points(case, gpu_lib):
         check_close(to_f64(lse[b, h]), ref_lse, dt, f"lse[{b},{h}]")
         for nm, got, r in zip(("dq", "dk", "dv"), (dq, dk, dv), O.attention_backward(qs, ks, vs, dos)):
             check_close(to_f64(got[b, h]), r, dt, f"{nm}[{b},{h}]")
+
+
+# The forward's key-range split (lh_forward on causal grids too small to
+# balance: the query blocks with more key tiles than the mean load of a
+# resident workgroup slot run as two chunks, merged by a second kernel).
+# Dense layers (L = 1, so the subsequence is the token sequence itself) are
+# compared with the oracle's float64 causal attention and with the unsplit
+# kernel of lh_attention on the same subsequence.  The small cases split every
+# block of two or more tiles, with lengths that put a block's diagonal in
+# either chunk and leave waves of a chunk with no visible keys; the 16-head
+# cases split only the heavier blocks (both kinds of item in one grid).
+SPLIT_CASES = [(64, 1, 3), (64, 63, 3), (64, 64, 3), (64, 65, 3), (64, 127, 3), (64, 129, 3),
+               (64, 300, 3), (64, 1000, 3), (64, 4000, 3), (128, 1, 3), (128, 130, 3),
+               (128, 257, 3), (128, 513, 3), (128, 900, 3), (128, 2500, 16), (64, 4000, 16)]
+
+
+@pytest.mark.parametrize("d,S,H", SPLIT_CASES, ids=[f"d{d}_S{s}_H{h}" for d, s, h in SPLIT_CASES])
+def test_forward_key_split(d, S, H, gpu_lib):
+    lb = gpu_lib
+    B = 1
+    print(f"[attention split] S={S} d={d} H={H}", flush=True)
+    rng = np.random.default_rng(1000 * d + S + H)
+    host = {t: synth.bf16_bits_from_f32(rng.standard_normal((B, H, S, d), dtype=np.float32))
+            for t in ("q", "k", "v")}
+    dev = {t: to_device(a, "bf16") for t, a in host.items()}
+    out, bufs, shape = lb.forward(dev["q"], dev["k"], dev["v"], 2, 1, S)
+    os2 = torch.empty(B, H, S, d, dtype=torch.float32, device="cuda")
+    lse2 = torch.empty(B, H, S, dtype=torch.float32, device="cuda")
+    lb.lh_attention(shape, bufs.qs, bufs.ks, bufs.vs, os2, lse2)
+    torch.cuda.synchronize()
+    for h in sorted({0, H // 2, H - 1}):
+        ref, ref_lse = O.attention(*(O.to_f64(host[t][0, h], "bf16") for t in ("q", "k", "v")))
+        check_close(to_f64(bufs.os[0, h]), ref, "bf16", f"os[0,{h}]")
+        check_close(to_f64(bufs.lse[0, h]), ref_lse, "bf16", f"lse[0,{h}]")
+        # split and unsplit differ only in where each chunk's weights are rounded
+        dos = float(np.max(np.abs(to_f64(bufs.os[0, h]) - to_f64(os2[0, h]))))
+        assert dos <= 4e-3 * float(np.max(np.abs(ref))), f"os split vs unsplit: {dos}"
+        dl = float(np.max(np.abs(to_f64(bufs.lse[0, h]) - to_f64(lse2[0, h]))))
+        assert dl <= 4e-3, f"lse split vs unsplit: {dl}"
