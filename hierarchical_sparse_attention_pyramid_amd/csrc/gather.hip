@@ -19,15 +19,19 @@
 // starts of `sel` once, then take one (entry, level) pair each, so the
 // dependent loads of the rank searches run as short chains in parallel.  A
 // rank search narrows to a window of `stride` entries with samples of `sel`
-// staged in LDS (every stride-th entry), then quarters that window in global
-// memory (three pivots per round trip; `sel` is small and stays cached) and
-// counts the last <= 16 entries directly.  The source rows are loaded before
+// staged in LDS (every stride-th entry, as dense as 2,048 samples allow: all
+// of `sel` up to 2,048 candidates, every 4th at 7,808), then quarters that
+// window in global memory (three pivots per round trip; `sel` is small and
+// stays cached; no round trip for windows of up to 16) and counts the last
+// <= 16 entries directly.  The source rows are loaded before
 // the searches (they follow from the entries alone) and stored after them.
 // The same block writes pos for the flat range from after the previous
 // block's last entry to its own last entry (to C for the last block; the
 // whole candidate range split evenly when K = 0): -1 everywhere first, then,
 // after those stores have completed and a barrier, the positions of its
 // entries.
+#include <algorithm>
+
 #include "kernels.h"
 
 namespace lh {
@@ -37,6 +41,9 @@ namespace {
 constexpr int kEntries = 64;      // subsequence positions per block
 constexpr int kThreads = 256;     // four (entry, level) pairs per entry at a time
 constexpr int kMaxSamples = 2048; // staged samples of sel
+#ifndef LH_GATHER_MINSTRIDE
+#define LH_GATHER_MINSTRIDE 1
+#endif
 
 struct Ranker {
   const int32_t* a;      // sorted ascending, n entries
@@ -97,7 +104,18 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(
   const int32_t n = i0 < g.K ? (int32_t)min<int64_t>(kEntries, g.K - i0) : 0;
   const Ranker r{sl, samp, g.K, ns, stride};
 
-  for (int i = tid; i < ns; i += kThreads) samp[i] = sl[(int64_t)i * stride];
+  {  // every sample load of a thread in flight before its first LDS store
+    constexpr int kPer = kMaxSamples / kThreads;
+    int32_t sv[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int i = tid + k * kThreads;
+      sv[k] = i < ns ? sl[(int64_t)i * stride] : 0;
+    }
+#pragma unroll
+    for (int k = 0; k < kPer; ++k)
+      if (tid + k * kThreads < ns) samp[tid + k * kThreads] = sv[k];
+  }
   if (tid < g.L) {
     s_base[tid] = g.base[tid];
     s_pw[tid] = g.pw[tid];
@@ -246,9 +264,10 @@ hipError_t launch_gather(const int32_t* sel, const void* const qkv[3], const Lay
                          const void* const pyr[3], int32_t* sub_idx, int32_t* pos,
                          void* const sub[3], const Geo& g, int dtype, int64_t BH, hipStream_t st) {
   if (g.S == 0) return hipSuccess;
-  // sample stride: at least 64, and at most kMaxSamples samples
+  // sample stride: the smallest that keeps at most kMaxSamples samples (1,
+  // all of sel in LDS, up to 2,048 candidates), at least LH_GATHER_MINSTRIDE
   const int64_t K = g.K;
-  const int64_t stride = K / kMaxSamples + 1 > 64 ? K / kMaxSamples + 1 : 64;
+  const int64_t stride = std::max<int64_t>(LH_GATHER_MINSTRIDE, (K + kMaxSamples - 1) / kMaxSamples);
   const int32_t ns = (int32_t)((K + stride - 1) / stride);
   const dim3 grid((unsigned)((g.S + kEntries - 1) / kEntries), (unsigned)BH);
   if (dtype == 1)
