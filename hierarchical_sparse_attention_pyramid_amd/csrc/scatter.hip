@@ -137,15 +137,19 @@ __global__ __launch_bounds__(256) void bcast_kernel(BcastArgs a) {
 // level; here every load of a row group is issued ahead of its use:
 //   * the workgroup first stages in LDS the positions of its tokens and of
 //     all their ancestors (one coalesced burst);
-//   * a row group covers 64 tokens (64 divides every p^l >= 64), so the
-//     "outer" levels with p^l >= 64 contribute the same rows to all of its
-//     tokens: they are summed once, their loads issued together;
+//   * a row group covers TOK tokens (64; 32 or 16 when 64 would leave fewer
+//     than 1,024 workgroups, which also shortens each group's chain of
+//     chunks; TOK divides every p^l >= TOK), so the "outer" levels with
+//     p^l >= TOK contribute the same rows to all of its tokens: they are
+//     summed once, their loads issued together;
 //   * the (at most two) inner levels change at chunk starts only (chunks of
 //     4 tokens, p >= 4); the rows of chunk c+1 (level 0 and the inner levels
 //     that change there) are loaded before chunk c is stored, from two
 //     alternating register buffers.
 // One tensor per row group (gridDim.z = number of tensors).
-constexpr int kFastTok = 64;
+#ifndef LH_BC_FAST_TOK
+#define LH_BC_FAST_TOK 0  // 0: chosen per launch; else forced (16, 32 or 64)
+#endif
 constexpr int kFastU = 4;
 constexpr int kFastInner = 2;      // inner levels handled (p = 4: levels 1, 2)
 constexpr int kFastOuter = 8;      // outer levels summed with loads in flight together
@@ -158,8 +162,10 @@ struct FastBuf {
   int si[kFastInner];
 };
 
-template <typename Tout, int SH>
+template <typename Tout, int SH, int TOK>
 __global__ __launch_bounds__(256) void bcast_fast(BcastArgs a) {
+  constexpr int kFastTok = TOK;
+  static_assert(TOK == 16 || TOK == 32 || TOK == 64, "row-group token counts");
   const Geo& g = a.g;
   const int lpr = g.d / kE;
   const int rgs = 256 / lpr;
@@ -179,7 +185,7 @@ __global__ __launch_bounds__(256) void bcast_fast(BcastArgs a) {
   // entries from entry B0 / p^l; at most 256 for l >= 1 since BT <= 1024 and
   // p >= 4).  A thread issues every position load it makes before its first
   // LDS store: the staging costs one memory latency, not one per level.
-  const int lbt = __builtin_ctz(BT);  // BT is a power of two (64 tokens x 8 or 16 row groups)
+  const int lbt = __builtin_ctz(BT);  // BT is a power of two (TOK tokens x 8 or 16 row groups)
   {
     constexpr int kTok = 1024 / 256;  // level-0 entries per thread
     int32_t p0[kTok], pl[kMaxLevels];
@@ -218,9 +224,10 @@ __global__ __launch_bounds__(256) void bcast_fast(BcastArgs a) {
   Tout* out = static_cast<Tout*>(a.out[z]) + a.lout.head(bh) + kE * lane;
   const bool mean = a.mean != 0;
 
-  // levels 1 .. lam-1 are inner (p^l < 64), lam .. L-1 outer
+  // levels 1 .. lam-1 are inner (p^l < TOK), lam .. L-1 outer
+  constexpr int kLogTok = TOK == 64 ? 6 : TOK == 32 ? 5 : 4;
   int lam = 1;
-  while (lam < g.L && (lg * lam) < 6) ++lam;
+  while (lam < g.L && (lg * lam) < kLogTok) ++lam;
   const int nin = lam - 1;  // <= 2 since p >= 4
 
   auto level_pos = [&](int l, int32_t j) { return sp[soff[l] + (j - (B0 >> (lg * l)))]; };
@@ -362,14 +369,33 @@ hipError_t launch_bcast(const BcastArgs& a, int dtype, int ntensors, int64_t BH,
   if (ntensors < 1 || ntensors > 3) return hipErrorInvalidValue;
   if (a.shift != 0 && (ntensors != 1 || a.mean == 0)) return hipErrorInvalidValue;
   if (LH_BC_FAST && a.g.log2p >= 2) {
-    const int64_t bt = (int64_t)rgs * kFastTok;
-    const dim3 grid((unsigned)((nv + bt - 1) / bt), (unsigned)BH, (unsigned)ntensors);
+    // tokens per row group: 64 unless that leaves under 1,024 workgroups
+    int tok = 64;
+    auto blocks = [&](int t) { return (nv + (int64_t)rgs * t - 1) / ((int64_t)rgs * t); };
+    if (LH_BC_FAST_TOK != 0) tok = LH_BC_FAST_TOK;
+    else while (tok > 16 && blocks(tok) * BH * ntensors < 1024) tok /= 2;
+    const dim3 grid((unsigned)blocks(tok), (unsigned)BH, (unsigned)ntensors);
+    auto go = [&](auto kern) { kern<<<grid, 256, 0, st>>>(a); };
     if (dtype == 1) {
-      if (a.shift) bcast_fast<__bf16, 1><<<grid, 256, 0, st>>>(a);
-      else bcast_fast<__bf16, 0><<<grid, 256, 0, st>>>(a);
+      if (a.shift) {
+        if (tok == 64) go(bcast_fast<__bf16, 1, 64>);
+        else if (tok == 32) go(bcast_fast<__bf16, 1, 32>);
+        else go(bcast_fast<__bf16, 1, 16>);
+      } else {
+        if (tok == 64) go(bcast_fast<__bf16, 0, 64>);
+        else if (tok == 32) go(bcast_fast<__bf16, 0, 32>);
+        else go(bcast_fast<__bf16, 0, 16>);
+      }
     } else {
-      if (a.shift) bcast_fast<float, 1><<<grid, 256, 0, st>>>(a);
-      else bcast_fast<float, 0><<<grid, 256, 0, st>>>(a);
+      if (a.shift) {
+        if (tok == 64) go(bcast_fast<float, 1, 64>);
+        else if (tok == 32) go(bcast_fast<float, 1, 32>);
+        else go(bcast_fast<float, 1, 16>);
+      } else {
+        if (tok == 64) go(bcast_fast<float, 0, 64>);
+        else if (tok == 32) go(bcast_fast<float, 0, 32>);
+        else go(bcast_fast<float, 0, 16>);
+      }
     }
     return hipGetLastError();
   }
