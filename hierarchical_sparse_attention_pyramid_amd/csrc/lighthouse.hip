@@ -186,7 +186,11 @@ lh_status make_plan(const lh_shape* s, Plan& P) {
   P.nstages = 0;
   P.sums_rows[0] = P.sums_rows[1] = 0;
   if (s->L == 1) {
-    P.st[P.nstages++] = Stage{0, 0, 64, 0, s->N, s->N, nvb, nvb, -1};
+    // scores only, no level to form: chunks shrink like the token passes'
+    // below, down to one row
+    int chunk = LH_POOL_TOKCHUNK;
+    while (chunk > 1 && BH * (s->N / chunk) < kPoolRowGroupsWanted) chunk /= 2;
+    P.st[P.nstages++] = Stage{0, 0, chunk, 0, s->N, s->N, nvb, nvb, -1};
   } else {
     const int lm = lam_max(s->p);
     int lvl = 0;
