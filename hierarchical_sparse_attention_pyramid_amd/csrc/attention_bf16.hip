@@ -21,6 +21,7 @@
 // (dQ; queries stationary), both atomic-free, recomputing P from the stored
 // log-sum-exp.
 #include <algorithm>
+#include <atomic>
 #include <type_traits>
 #include <vector>
 
@@ -1036,17 +1037,19 @@ namespace {
 // (compute units x workgroups per unit), looked up once per device.
 template <typename Kern>
 int64_t resident_slots(Kern kern, int threads) {
-  static int64_t cache[64];
+  static std::atomic<int64_t> cache[64];  // host threads may race to fill it: same value
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  if (cache[dev] == 0) {
+  int64_t v = cache[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
     int cus = 0, per = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kern, threads, 0) != hipSuccess)
       return 0;
-    cache[dev] = (int64_t)cus * per;
+    v = (int64_t)cus * per;
+    cache[dev].store(v, std::memory_order_relaxed);
   }
-  return cache[dev];
+  return v;
 }
 
 #ifndef LH_FWD_SPLIT
@@ -1096,12 +1099,10 @@ hipError_t fwd_bf16(const __bf16* Q, const __bf16* K, const __bf16* V, float* o,
   using C = FwdCfg<D, QW, WAVES>;
   auto kern = attn_fwd_bf16<D, QW, WAVES, MINW>;
   const int64_t nb = (S + C::kQB - 1) / C::kQB;
-  FwdSplit sp;
+  FwdSplit sp{};
   sp.o = sb ? sb->o : nullptr;
   sp.lam = sb ? sb->lam : nullptr;
-  int64_t b0 = nb;
-  if (sb) b0 = plan_split(S, nb, C::kQB, BH, resident_slots(kern, C::kThreads), sp);
-  else sp.n = 0;
+  const int64_t b0 = sb ? plan_split(S, nb, C::kQB, BH, resident_slots(kern, C::kThreads), sp) : nb;
   const bool pr = sp.n == 0 && LH_PAIR_FWD && pair_blocks(nb, BH);
   const int64_t grid = sp.n > 0 ? sp.n * BH : causal_grid(nb, BH, pr);
   kern<<<dim3((unsigned)grid), C::kThreads, 0, st>>>(Q, K, V, o, lse, (int)S, sl2, pr ? 1 : 0, sp);
