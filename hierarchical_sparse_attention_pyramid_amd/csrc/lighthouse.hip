@@ -283,6 +283,9 @@ lh_status check_ws(void* ws, size_t have, size_t need) {
   if (!ws) return fail(LH_EINVAL, "workspace pointer is null");
   if (have < need)
     return fail(LH_EWORKSPACE, "workspace too small: need " + std::to_string(need) + " bytes");
+  // its regions start at multiples of 256 bytes from ws and are read and
+  // written in 16-byte vectors
+  if (reinterpret_cast<uintptr_t>(ws) % 16) return fail(LH_EINVAL, "workspace must be 16-byte aligned");
   return LH_OK;
 }
 

@@ -147,6 +147,9 @@ typedef struct {
 } lh_buffers;
 
 /* Sizes of every buffer and workspace for a shape.  Host only; no GPU call.
+ * A workspace (ws) is caller-owned device memory of at least the stated
+ * size, 16-byte aligned (LH_EINVAL otherwise), whose contents need not be
+ * initialised and are not kept between calls.
  * Returns LH_EINVAL / LH_EUNSUPPORTED for shapes the library rejects. */
 lh_status lh_query_sizes(const lh_shape *shape, lh_sizes *out);
 

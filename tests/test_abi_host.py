@@ -89,6 +89,16 @@ def test_null_pointers_and_small_workspace_are_rejected_without_a_gpu(lb):
     assert st == 1 and b"buffers" in lib.lh_last_error()
 
 
+def test_misaligned_workspace_is_rejected_without_a_gpu(lb):
+    lib = lb.load_library()
+    big = lb.make_shape(1, 2, 98304, 64, 4, 5, 8192, 1)
+    zb = lb.lh_query_sizes(big)
+    # nothing is launched: the workspace check fails first
+    st = lib.lh_topk(ctypes.byref(big), 4096, 4096, 4096 + 8, zb.ws_topk, None)
+    assert st == 1 and b"16-byte aligned" in lib.lh_last_error()
+    assert lib.lh_topk(ctypes.byref(big), 4096, 4096, 4096 + 256, zb.ws_topk - 1, None) == 3
+
+
 def _strided(lb, qkv=None, out=None, B=2, H=4, N=256, d=64, dtype=1):
     return lb.make_shape(B, H, N, d, 4, 3, 40, dtype, qkv, out)
 
