@@ -128,3 +128,39 @@ def test_many_heads(dt, gpu_lib):
         g = O.backward_head(host["dout"][b, h], f, p, L, dt)
         for nm, got, ref in zip(("dq", "dk", "dv"), (dq, dk, dv), g):
             check_close(to_f64(got[b, h]), ref, dt, f"{nm}[{b},{h}]")
+
+
+# A one-entry subsequence: N = p^(L-1), so the coarsest level holds one entry
+# and S = 1 keeps only it.  Its softmax weight is identically 1, so dq and dk
+# are exactly zero in the mathematics (the oracle's are 0) while the output
+# and dv are not.  A relative bar has no scale there, so dq and dk are held to
+# zero on the scale of dv; their values on the GPU are rounding noise of the
+# backward's dP - rowsum(dO*O).
+@pytest.mark.parametrize("mode", ["span", "causal"])
+@pytest.mark.parametrize("dt,d,p,L", [("bf16", 64, 6, 4), ("fp32", 64, 6, 4), ("bf16", 128, 4, 3)])
+def test_one_entry_subsequence(dt, d, p, L, mode, gpu_lib):
+    lb = gpu_lib
+    B, H = 2, 2
+    N, S = p ** (L - 1), 1
+    print(f"[robust] one entry: N={N} p={p} L={L} d={d} {dt} {mode}", flush=True)
+    host = {}
+    for t in ("q", "k", "v", "dout"):
+        a = np.stack([np.stack([synth.head_tensor(4242, t, b, h, N, d) for h in range(H)])
+                      for b in range(B)])
+        host[t] = synth.bf16_bits_from_f32(a) if dt == "bf16" else a
+    dev = {t: to_device(a, dt) for t, a in host.items()}
+    out, bufs, shape = lb.forward(dev["q"], dev["k"], dev["v"], p, L, S, scatter=mode)
+    dq, dk, dv = lb.backward(shape, dev["dout"], bufs)
+    torch.cuda.synchronize()
+    for b in range(B):
+        for h in range(H):
+            f = O.forward_head(host["q"][b, h], host["k"][b, h], host["v"][b, h], p, L, S, dt, mode)
+            np.testing.assert_array_equal(bufs.pos[b, h].cpu().numpy(), f["pos"])
+            check_close(to_f64(out[b, h]), O.to_f64(f["out"], dt), dt, f"out[{b},{h}]")
+            rq, rk, rv = O.backward_head(host["dout"][b, h], f, p, L, dt)
+            assert np.max(np.abs(rq)) == 0.0 and np.max(np.abs(rk)) == 0.0  # the oracle
+            check_close(to_f64(dv[b, h]), rv, dt, f"dv[{b},{h}]")
+            scale = float(np.max(np.abs(rv)))
+            for name, g in (("dq", dq), ("dk", dk)):
+                err = float(torch.max(torch.abs(g[b, h].float())))
+                assert err <= 1e-4 * scale, f"{name}[{b},{h}]: {err} against dv scale {scale}"
